@@ -1,0 +1,16 @@
+"""CPU oracle of the Parallax attention forward pass (test infrastructure only).
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline
+leg may import this package; the product path never does.
+"""
+from .parallax_oracle import (  # noqa: F401
+    decode,
+    decode_explicit,
+    decode_stream,
+    explicit_row,
+    prefill,
+    prefill_explicit,
+    prefill_head,
+    prefill_rows,
+    softmax_weights,
+)

@@ -1,0 +1,218 @@
+"""CPU oracle for the Parallax attention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package's smoke check and
+the benchmark's CPU-baseline leg may import this module.  The product path (the
+HIP library and its Python binding) never imports, links or calls it, and it
+shares no code with that path.
+
+Source: the page "Parallax - Parameterized Local Linear Attention for Language
+Modeling" (technical summary, Korean and German editions on gist.science):
+  * section "Core mechanism", Eq. 2: the output is softmax attention minus the
+    per-query KV covariance matrix applied to the probe, o_i = o^SA_i - Sigma_KV^(i) rho_i;
+  * section "Core mechanism", Eq. 1: the probe rho_i = W_R x_i comes from the
+    layer input; here it is an input array;
+  * section "Core mechanism", design choices: the boundary-amplification factor
+    eta_i is fixed to zero, and no per-token solver is used;
+  * section "Problem": softmax attention is the local-constant (Nadaraya-Watson)
+    estimator, whose weights are the softmax of the scaled scores;
+  * section "Significance": W_R = 0 turns the layer back into ordinary softmax
+    attention (the rho = 0 special case);
+  * section "Results": a gate value scales the correction branch.
+
+Readings taken where the pages are silent (each is listed in the design doc):
+  * Sigma_KV^(i) is the cross-covariance of values and keys under the causal
+    softmax weights w_ij of query i, centred at the weighted means, weights
+    summing to one, no Bessel factor; it is d_v x d_k so that it acts on
+    rho_i in R^{d_k}.
+  * Scores are s_ij = scale <q_i, k_j> with scale = 1/sqrt(d_k) unless given;
+    the probe products r_ij = <rho_i, k_j> are unscaled.
+  * The gate g_h is a per-head scalar on the correction:
+    o_i = o^SA_i - g_h Sigma_KV^(i) rho_i.
+  * Prefill is causal with the diagonal included (j <= i); decode attends the
+    first seqlens[b] cached keys, and a sequence of length zero gives zeros.
+
+Everything is computed in float64 from the exact values of the inputs (an
+up-cast of bf16 or fp32 to fp64 is exact).  There is no tie-break, argmax or
+iteration, so every output element has exactly one correct value.
+
+Two forms are provided:
+  * the explicit form builds Sigma_KV^(i) as a d_v x d_k matrix per query
+    (`explicit_row`, `prefill_explicit`, `decode_explicit`);
+  * the expanded form uses the identity
+      Sigma^(i) rho_i = sum_j w_ij r_ij v_j - o^SA_i sum_j w_ij r_ij
+    with r_ij = <rho_i, k_j>, evaluated with whole-row matrix products
+    (`prefill`, `decode`).
+Both are pinned by the CPU tests against library routines, closed forms and
+invariants; they are not only compared with each other.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    """Exact up-cast of an array-like (numpy or a CPU torch tensor) to fp64."""
+    if hasattr(x, "detach"):
+        x = x.detach().cpu()
+        if str(x.dtype) in ("torch.bfloat16", "torch.float16"):
+            x = x.float()
+        x = x.double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def softmax_weights(q_i, K, scale):
+    """Nadaraya-Watson weights of one query over the keys K [n, d_k]:
+    w_j = softmax_j(scale <q_i, k_j>) (page section "Problem")."""
+    s = scale * (K @ q_i)
+    e = np.exp(s - s.max())
+    return e / e.sum()
+
+
+def explicit_row(q_i, K, V, rho_i, g, scale):
+    """One output row by the explicit covariance form of Eq. 2.
+
+    K [n, d_k], V [n, d_v] are the keys and values the query attends.  Returns
+    (o_plx, o_sa, Sigma) with Sigma the d_v x d_k weighted cross-covariance
+    sum_j w_j (v_j - o_sa)(k_j - kbar)^T.
+    """
+    q_i, K, V, rho_i = _f64(q_i), _f64(K), _f64(V), _f64(rho_i)
+    w = softmax_weights(q_i, K, scale)
+    o_sa = w @ V
+    kbar = w @ K
+    sigma = (V - o_sa).T @ (w[:, None] * (K - kbar))
+    return o_sa - g * (sigma @ rho_i), o_sa, sigma
+
+
+def _default_scale(d_k, scale):
+    return 1.0 / np.sqrt(d_k) if scale is None else float(scale)
+
+
+def prefill_explicit(q, k, v, rho, gate, scale=None):
+    """Causal prefill, every row by the explicit form.  q, k, rho [B,H,L,d_k],
+    v [B,H,L,d_v], gate [H].  Cost O(L^2 d^2) per head: small inputs only."""
+    q, k, v, rho, gate = map(_f64, (q, k, v, rho, gate))
+    B, H, L, dk = q.shape
+    sc = _default_scale(dk, scale)
+    out = np.zeros(v.shape[:3] + (v.shape[3],), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for i in range(L):
+                out[b, h, i] = explicit_row(q[b, h, i], k[b, h, : i + 1],
+                                            v[b, h, : i + 1], rho[b, h, i],
+                                            gate[h], sc)[0]
+    return out
+
+
+def prefill_head(q, k, v, rho, g, scale, rows=None, block=512):
+    """Expanded form for one head: q, k, rho [L, d_k], v [L, d_v].
+
+    Returns the output rows listed in `rows` (default: all), each attending
+    keys 0..i.  Rows are processed a block at a time only to bound memory; each
+    row is computed from its own scores exactly as in the definition.
+    """
+    L = q.shape[0]
+    rows = np.arange(L) if rows is None else np.asarray(rows)
+    out = np.empty((rows.size, v.shape[1]), dtype=np.float64)
+    for s0 in range(0, rows.size, block):
+        r = rows[s0: s0 + block]
+        n = int(r.max()) + 1
+        S = scale * (q[r] @ k[:n].T)                      # [rows, n] scores
+        causal = np.arange(n)[None, :] <= r[:, None]
+        S = np.where(causal, S, -np.inf)
+        W = np.exp(S - S.max(axis=1, keepdims=True))
+        W /= W.sum(axis=1, keepdims=True)                 # softmax weights w_ij
+        R = rho[r] @ k[:n].T                              # r_ij = <rho_i, k_j>
+        WR = W * R
+        o_sa = W @ v[:n]                                  # sum_j w_ij v_j
+        u = WR @ v[:n]                                    # sum_j w_ij r_ij v_j
+        rbar = WR.sum(axis=1, keepdims=True)              # sum_j w_ij r_ij
+        out[s0: s0 + r.size] = o_sa - g * (u - o_sa * rbar)
+    return out
+
+
+def prefill(q, k, v, rho, gate, scale=None, heads=None):
+    """Causal prefill by the expanded form.  Same layouts as prefill_explicit.
+    `heads` optionally restricts the work to a list of (b, h) pairs; the other
+    heads of the returned array are left as NaN."""
+    q, k, v, rho, gate = map(_f64, (q, k, v, rho, gate))
+    B, H, L, dk = q.shape
+    sc = _default_scale(dk, scale)
+    out = np.full(v.shape, np.nan, dtype=np.float64)
+    todo = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b, h in todo:
+        out[b, h] = prefill_head(q[b, h], k[b, h], v[b, h], rho[b, h], gate[h], sc)
+    return out
+
+
+def prefill_rows(q, k, v, rho, gate, b, h, rows, scale=None):
+    """Selected causal output rows of head (b, h), by the explicit form."""
+    dk = q.shape[-1]
+    sc = _default_scale(dk, scale)
+    g = float(_f64(gate)[h])
+    res = []
+    for i in rows:
+        i = int(i)
+        res.append(explicit_row(q[b, h, i], k[b, h, : i + 1], v[b, h, : i + 1],
+                                rho[b, h, i], g, sc)[0])
+    return np.stack(res)
+
+
+def decode_stream(q, K, V, rho, g, scale):
+    """Expanded form for one decode query over all keys K [n, d_k], V [n, d_v]
+    (no mask: the cache holds exactly the keys the query attends).  n = 0
+    gives a zero row."""
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1], dtype=np.float64)
+    s = scale * (K @ q)
+    w = np.exp(s - s.max())
+    w /= w.sum()
+    r = K @ rho
+    o_sa = w @ V
+    u = (w * r) @ V
+    rbar = (w * r).sum()
+    return o_sa - g * (u - o_sa * rbar)
+
+
+def _lens(seqlens, Lmax):
+    sl = _f64(seqlens).astype(np.int64)
+    return np.clip(sl, 0, Lmax)
+
+
+def decode(q, kcache, vcache, rho, gate, seqlens, scale=None, streams=None):
+    """One decode step by the expanded form.  q, rho [B,H,d_k];
+    kcache [B,H,Lmax,d_k]; vcache [B,H,Lmax,d_v]; seqlens [B]; gate [H].
+    Sequence b attends cache positions 0..seqlens[b]-1 (clamped to
+    [0, Lmax]).  `streams` optionally restricts the work to (b, h) pairs; the
+    rest of the output is NaN.  Cache rows are up-cast per stream."""
+    B, H, Lmax, dk = kcache.shape
+    dv = vcache.shape[-1]
+    sc = _default_scale(dk, scale)
+    qf, rf, gf = _f64(q), _f64(rho), _f64(gate)
+    lens = _lens(seqlens, Lmax)
+    out = np.full((B, H, dv), np.nan, dtype=np.float64)
+    todo = [(b, h) for b in range(B) for h in range(H)] if streams is None else streams
+    for b, h in todo:
+        n = int(lens[b])
+        K = _f64(kcache[b, h, :n])
+        V = _f64(vcache[b, h, :n])
+        out[b, h] = decode_stream(qf[b, h], K, V, rf[b, h], gf[h], sc)
+    return out
+
+
+def decode_explicit(q, kcache, vcache, rho, gate, seqlens, scale=None, streams=None):
+    """One decode step with Sigma_KV built explicitly per stream."""
+    B, H, Lmax, dk = kcache.shape
+    dv = vcache.shape[-1]
+    sc = _default_scale(dk, scale)
+    qf, rf, gf = _f64(q), _f64(rho), _f64(gate)
+    lens = _lens(seqlens, Lmax)
+    out = np.full((B, H, dv), np.nan, dtype=np.float64)
+    todo = [(b, h) for b in range(B) for h in range(H)] if streams is None else streams
+    for b, h in todo:
+        n = int(lens[b])
+        if n == 0:
+            out[b, h] = 0.0
+            continue
+        out[b, h] = explicit_row(qf[b, h], _f64(kcache[b, h, :n]), _f64(vcache[b, h, :n]),
+                                 rf[b, h], gf[h], sc)[0]
+    return out
