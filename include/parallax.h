@@ -1,0 +1,150 @@
+/*
+ * parallax.h - C ABI of the Parallax attention forward pass on AMD CDNA4 (gfx950).
+ *
+ * The operation is defined on the page "Parallax - Parameterized Local Linear
+ * Attention for Language Modeling" (technical summary; section "Core
+ * mechanism", Eq. 2):
+ *
+ *     o_i = o^SA_i - g_h * Sigma_KV^(i) rho_i
+ *
+ * o^SA_i is causal softmax attention with weights w_ij = softmax_j(scale <q_i,k_j>),
+ * Sigma_KV^(i) is the d x d cross-covariance of (v_j, k_j) under those weights
+ * (centred, weights summing to one), rho_i is the probe (Eq. 1, rho_i = W_R x_i,
+ * supplied here as an input), the boundary factor eta_i is zero and no solver
+ * is involved (same section, design choices), and g_h is a per-head gate on
+ * the correction branch (section "Results").  The kernels evaluate the
+ * covariance term without forming the matrix, through
+ *     Sigma^(i) rho_i = sum_j w_ij r_ij v_j - o^SA_i sum_j w_ij r_ij,  r_ij = <rho_i,k_j>,
+ * in one streaming pass over K and V shared by both branches (section
+ * "Hardware-aware algorithm").
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers to contiguous row-major arrays,
+ *     16-byte aligned.  The caller owns every buffer; the library keeps no
+ *     pointer after a call returns and never frees caller memory.
+ *   - d (head dimension, d_k = d_v) must be 64 or 128.
+ *   - dtype is PLX_BF16 (inputs stored as bfloat16) or PLX_F32.  Outputs are
+ *     always fp32.  scale multiplies <q,k> only; pass scale <= 0 for 1/sqrt(d).
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously; device faults surface at the caller's
+ *     next synchronisation.
+ *   - Arguments are validated before anything is enqueued.  On a bad argument
+ *     the call returns an error status, enqueues nothing and sets the text of
+ *     parallax_last_error().  A failed launch or allocation returns PLX_EHIP /
+ *     PLX_ENOMEM.  The library never aborts, prints or throws across the ABI.
+ *   - Apart from the per-thread error text the library has no mutable global
+ *     state; calls from several host threads are safe.
+ */
+#ifndef PARALLAX_H
+#define PARALLAX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PARALLAX_ABI_VERSION 1
+
+typedef enum {
+  PLX_OK = 0,
+  PLX_EINVAL = 1,        /* null pointer, non-positive size, workspace too small */
+  PLX_EUNSUPPORTED = 2,  /* d not in {64,128}, unknown dtype */
+  PLX_ENOMEM = 3,        /* the library could not allocate its own workspace */
+  PLX_EHIP = 4           /* a HIP runtime call or kernel launch failed */
+} plx_status;
+
+typedef enum { PLX_F32 = 0, PLX_BF16 = 1 } plx_dtype;
+
+/* ABI version of the loaded library (PARALLAX_ABI_VERSION at build time). */
+int parallax_abi_version(void);
+
+/* Text of the last error on the calling thread ("" if none).  Valid until the
+ * next library call on the same thread. */
+const char* parallax_last_error(void);
+
+/* ------------------------------------------------------------------ prefill
+ * Causal prefill (page section "Core mechanism", Eq. 2, with query i attending
+ * keys 0..i).
+ *   q, k, v, rho : [B, H, L, d] in dtype
+ *   gate         : [H] fp32, the correction gate g_h
+ *   out          : [B, H, L, d] fp32
+ * workspace: device scratch of at least parallax_prefill_workspace_bytes()
+ * bytes (0 for PLX_F32).  If workspace is NULL the library allocates and frees
+ * it on `stream` (stream-ordered allocation).  In PLX_BF16 mode the workspace
+ * holds V converted to fp16 in a per-64-key-tile transposed layout (see
+ * parallax_prefill_stage_v); the conversion is exact for |v| in
+ * [2^-14, 65504] and values must stay below 65504 in magnitude. */
+size_t parallax_prefill_workspace_bytes(int B, int H, int L, int d, int dtype);
+
+int parallax_prefill(const void* q, const void* k, const void* v, const void* rho,
+                     const float* gate, float* out,
+                     int B, int H, int L, int d, float scale, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two stages of a PLX_BF16 prefill, for callers that keep the staged V
+ * (for example across several calls over the same keys).
+ * stage_v: v [B,H,L,d] bf16 -> vt16, fp16, laid out [B*H][ceil(L/64)][d][64]
+ *          (64 consecutive keys of one feature contiguous), keys past L zero.
+ *          vt16 must hold parallax_prefill_workspace_bytes(B,H,L,d,PLX_BF16).
+ * attend : the fused causal forward pass reading V from vt16. */
+int parallax_prefill_stage_v(const void* v, void* vt16, int B, int H, int L, int d,
+                             void* stream);
+
+int parallax_prefill_attend(const void* q, const void* k, const void* vt16,
+                            const void* rho, const float* gate, float* out,
+                            int B, int H, int L, int d, float scale, void* stream);
+
+/* ------------------------------------------------------------------- decode
+ * One decode step per sequence (page section "Core mechanism", Eq. 2, the
+ * query attending every cached key of its sequence; section "Hardware-aware
+ * algorithm": both branches share one pass over the KV stream).
+ *   q, rho         : [B, H, d] in dtype
+ *   kcache, vcache : [B, H, Lmax, d] in dtype
+ *   gate           : [H] fp32
+ *   seqlens        : [B] int32 in device memory; sequence b attends cache
+ *                    positions 0..seqlens[b]-1.  Values are clamped to
+ *                    [0, Lmax] on the device; length 0 yields a zero row.
+ *                    Cache positions at or past seqlens[b] are never read.
+ *   out            : [B, H, d] fp32
+ * split_keys: keys per split of the split-KV pass (a multiple of 64, or 0 for
+ * the library's choice).  workspace: at least
+ * parallax_decode_workspace_bytes() bytes, or NULL to let the library allocate
+ * on `stream`. */
+size_t parallax_decode_workspace_bytes(int B, int H, int Lmax, int d, int split_keys);
+
+int parallax_decode(const void* q, const void* kcache, const void* vcache, const void* rho,
+                    const float* gate, float* out, const int32_t* seqlens,
+                    int B, int H, int Lmax, int d, float scale, int dtype, int split_keys,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two stages of a decode step.  They are also the merge point for a
+ * sequence whose keys are spread over several devices: partial states over
+ * disjoint key ranges combine exactly.
+ * partials: for each (b,h) and split s < ceil(seqlens[b]/split_keys), a record
+ *   of 2d+4 floats at partials + ((b*H+h)*S + s)*(2d+4), S = ceil(Lmax/split_keys):
+ *   [0] m = max_j scale*log2(e)*<q,k_j>       (base-2 log domain)
+ *   [1] l = sum_j 2^(scale*log2(e)*<q,k_j> - m)
+ *   [2] c = sum_j 2^(...) r_j,  r_j = <rho,k_j>
+ *   [3] unused
+ *   [4 .. 4+d)      sum_j 2^(...) v_j
+ *   [4+d .. 4+2d)   sum_j 2^(...) r_j v_j
+ *   split_keys must be given explicitly (no 0) and the same in both calls. */
+int parallax_decode_partials(const void* q, const void* kcache, const void* vcache,
+                             const void* rho, const int32_t* seqlens, float* partials,
+                             int B, int H, int Lmax, int d, float scale, int dtype,
+                             int split_keys, void* stream);
+
+int parallax_decode_combine(const float* partials, const float* gate, const int32_t* seqlens,
+                            float* out, int B, int H, int Lmax, int d, int split_keys,
+                            void* stream);
+
+/* The split size parallax_decode uses when split_keys is 0. */
+int parallax_decode_default_split(int B, int H, int Lmax, int d);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARALLAX_H */

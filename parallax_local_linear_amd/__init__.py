@@ -1,0 +1,193 @@
+"""Parallax attention forward pass on AMD MI355X (gfx950).
+
+The operation (page "Parallax - Parameterized Local Linear Attention for
+Language Modeling", section "Core mechanism", Eq. 2) is
+
+    o_i = o^SA_i - g_h * Sigma_KV^(i) rho_i
+
+softmax attention minus a gated correction: the softmax-weighted covariance of
+values and keys applied to the probe rho_i.  `prefill` runs the causal forward
+pass over whole sequences; `decode` runs one query per sequence against a KV
+cache.  Both are thin wrappers over the C ABI of libparallax.so: they check
+shapes, allocate outputs and workspaces with torch on the inputs' device, and
+enqueue the HIP kernels on torch's current stream.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from ._native import PLX_BF16, PLX_F32, ParallaxError, call, lib  # noqa: F401
+
+__all__ = ["prefill", "decode", "prefill_stage_v", "prefill_attend", "decode_partials",
+           "decode_combine", "prefill_workspace_bytes", "decode_workspace_bytes",
+           "decode_default_split", "ParallaxError"]
+
+_DT = {torch.bfloat16: PLX_BF16, torch.float32: PLX_F32}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check(name, t, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _scale(scale, d):
+    return float(scale) if scale is not None else 1.0 / math.sqrt(d)
+
+
+def prefill_workspace_bytes(B, H, L, d, dtype=torch.bfloat16) -> int:
+    return int(lib().parallax_prefill_workspace_bytes(B, H, L, d, _DT[dtype]))
+
+
+def decode_workspace_bytes(B, H, Lmax, d, split_keys=0) -> int:
+    return int(lib().parallax_decode_workspace_bytes(B, H, Lmax, d, split_keys))
+
+
+def decode_default_split(B, H, Lmax, d) -> int:
+    return int(lib().parallax_decode_default_split(B, H, Lmax, d))
+
+
+def prefill(q, k, v, rho, gate, scale=None, out=None, workspace=None):
+    """Causal Parallax prefill.  q, k, v, rho: [B, H, L, d] bf16 or fp32 on one
+    GPU; gate: [H] fp32.  Returns out [B, H, L, d] fp32."""
+    _check("q", q)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, L, d]")
+    B, H, L, d = q.shape
+    dt = q.dtype
+    if dt not in _DT:
+        raise TypeError(f"unsupported dtype {dt}")
+    for n, t in (("k", k), ("v", v), ("rho", rho)):
+        _check(n, t, dt, q.shape, q.device)
+    _check("gate", gate, torch.float32, (H,), q.device)
+    if out is None:
+        out = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
+    _check("out", out, torch.float32, (B, H, L, d), q.device)
+    wsb = 0
+    if workspace is None and dt == torch.bfloat16:
+        wsb = prefill_workspace_bytes(B, H, L, d, dt)
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+    elif workspace is not None:
+        _check("workspace", workspace, device=q.device)
+        wsb = workspace.numel() * workspace.element_size()
+    call("parallax_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(rho), _ptr(gate), _ptr(out),
+         B, H, L, d, _scale(scale, d), _DT[dt], _ptr(workspace), wsb, _stream(q.device))
+    return out
+
+
+def prefill_stage_v(v, vt=None):
+    """First stage of a bf16 prefill: V -> fp16 V^T tiles (a uint8 buffer)."""
+    _check("v", v, torch.bfloat16)
+    B, H, L, d = v.shape
+    n = prefill_workspace_bytes(B, H, L, d, torch.bfloat16)
+    if vt is None:
+        vt = torch.empty(n, dtype=torch.uint8, device=v.device)
+    _check("vt", vt, device=v.device)
+    if vt.numel() * vt.element_size() < n:
+        raise ValueError(f"vt must hold {n} bytes")
+    call("parallax_prefill_stage_v", _ptr(v), _ptr(vt), B, H, L, d, _stream(v.device))
+    return vt
+
+
+def prefill_attend(q, k, vt, rho, gate, scale=None, out=None):
+    """Second stage of a bf16 prefill, reading V from prefill_stage_v's buffer."""
+    _check("q", q, torch.bfloat16)
+    B, H, L, d = q.shape
+    for n, t in (("k", k), ("rho", rho)):
+        _check(n, t, torch.bfloat16, q.shape, q.device)
+    _check("gate", gate, torch.float32, (H,), q.device)
+    _check("vt", vt, device=q.device)
+    if vt.numel() * vt.element_size() < prefill_workspace_bytes(B, H, L, d):
+        raise ValueError("vt is too small")
+    if out is None:
+        out = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
+    _check("out", out, torch.float32, (B, H, L, d), q.device)
+    call("parallax_prefill_attend", _ptr(q), _ptr(k), _ptr(vt), _ptr(rho), _ptr(gate),
+         _ptr(out), B, H, L, d, _scale(scale, d), _stream(q.device))
+    return out
+
+
+def _decode_checks(q, kcache, vcache, rho, seqlens):
+    _check("q", q)
+    if q.dim() != 3 or kcache.dim() != 4:
+        raise ValueError("q must be [B, H, d] and kcache [B, H, Lmax, d]")
+    B, H, d = q.shape
+    Lmax = kcache.shape[2]
+    dt = q.dtype
+    if dt not in _DT:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check("rho", rho, dt, (B, H, d), q.device)
+    _check("kcache", kcache, dt, (B, H, Lmax, d), q.device)
+    _check("vcache", vcache, dt, (B, H, Lmax, d), q.device)
+    _check("seqlens", seqlens, torch.int32, (B,), q.device)
+    return B, H, Lmax, d, dt
+
+
+def decode(q, kcache, vcache, rho, gate, seqlens, scale=None, split_keys=0, out=None,
+           workspace=None):
+    """One Parallax decode step.  q, rho: [B, H, d]; kcache, vcache:
+    [B, H, Lmax, d] (bf16 or fp32); gate [H] fp32; seqlens [B] int32 on the
+    GPU.  Returns out [B, H, d] fp32."""
+    B, H, Lmax, d, dt = _decode_checks(q, kcache, vcache, rho, seqlens)
+    _check("gate", gate, torch.float32, (H,), q.device)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    _check("out", out, torch.float32, (B, H, d), q.device)
+    if workspace is None:
+        wsb = decode_workspace_bytes(B, H, Lmax, d, split_keys)
+        workspace = torch.empty(max(wsb, 4), dtype=torch.uint8, device=q.device)
+    _check("workspace", workspace, device=q.device)
+    wsb = workspace.numel() * workspace.element_size()
+    call("parallax_decode", _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(rho), _ptr(gate),
+         _ptr(out), _ptr(seqlens), B, H, Lmax, d, _scale(scale, d), _DT[dt], int(split_keys),
+         _ptr(workspace), wsb, _stream(q.device))
+    return out
+
+
+def decode_partials(q, kcache, vcache, rho, seqlens, split_keys, scale=None, partials=None):
+    """First stage of decode: per-split partial records [B, H, S, 2d+4] fp32."""
+    B, H, Lmax, d, dt = _decode_checks(q, kcache, vcache, rho, seqlens)
+    S = -(-Lmax // split_keys)
+    if partials is None:
+        partials = torch.empty((B, H, S, 2 * d + 4), dtype=torch.float32, device=q.device)
+    _check("partials", partials, torch.float32, (B, H, S, 2 * d + 4), q.device)
+    call("parallax_decode_partials", _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(rho),
+         _ptr(seqlens), _ptr(partials), B, H, Lmax, d, _scale(scale, d), _DT[dt],
+         int(split_keys), _stream(q.device))
+    return partials
+
+
+def decode_combine(partials, gate, seqlens, Lmax, split_keys, out=None):
+    """Second stage of decode: merge the partial records into out [B, H, d]."""
+    _check("partials", partials, torch.float32)
+    B, H, S, w = partials.shape
+    d = (w - 4) // 2
+    _check("gate", gate, torch.float32, (H,), partials.device)
+    _check("seqlens", seqlens, torch.int32, (B,), partials.device)
+    if S != -(-Lmax // split_keys):
+        raise ValueError("partials do not match Lmax / split_keys")
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.float32, device=partials.device)
+    _check("out", out, torch.float32, (B, H, d), partials.device)
+    call("parallax_decode_combine", _ptr(partials), _ptr(gate), _ptr(seqlens), _ptr(out), B, H,
+         Lmax, d, int(split_keys), _stream(partials.device))
+    return out

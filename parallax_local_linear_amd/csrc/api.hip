@@ -1,0 +1,283 @@
+// Host side of the Parallax C ABI: argument checks, workspace handling, launches.
+// Declarations, layouts and error rules are in include/parallax.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/parallax.h"
+
+namespace plx {
+hipError_t launch_stage_v(const void* v, void* vt, int BH, int L, int d, hipStream_t s);
+hipError_t launch_prefill_bf16(const void* q, const void* k, const void* vt, const void* rho,
+                               const float* gate, float* out, int B, int H, int L, int d,
+                               float scale, hipStream_t s);
+hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, const void* rho,
+                              const float* gate, float* out, int B, int H, int L, int d,
+                              float scale, hipStream_t s);
+hipError_t launch_decode_split(const void* q, const void* kc, const void* vc, const void* rho,
+                               const int* seqlens, float* part, int B, int H, int Lmax, int d,
+                               int C, float scale, bool bf16, hipStream_t s);
+hipError_t launch_decode_combine(const float* part, const float* gate, const int* seqlens,
+                                 float* out, int B, int H, int Lmax, int d, int C,
+                                 hipStream_t s);
+}  // namespace plx
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return PLX_OK;
+}
+
+int hip_fail(const char* what, hipError_t e) {
+  return fail(PLX_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kTileKeys = 64;
+constexpr long long kMaxElems = (1LL << 40);   // guard against size_t overflow of products
+
+bool dims_ok(int B, int H, int L, int d, const char* fn, const char* lname, int* status) {
+  if (B <= 0 || H <= 0 || L <= 0) {
+    *status = fail(PLX_EINVAL, "%s: B, H and %s must be positive (got %d, %d, %d)", fn, lname,
+                   B, H, L);
+    return false;
+  }
+  if (d != 64 && d != 128) {
+    *status = fail(PLX_EUNSUPPORTED, "%s: d must be 64 or 128 (got %d)", fn, d);
+    return false;
+  }
+  if ((long long)B * H * (long long)L * d > kMaxElems || (long long)L * d > (1LL << 31)) {
+    *status = fail(PLX_EINVAL, "%s: tensor too large", fn);
+    return false;
+  }
+  return true;
+}
+
+// The decode grid puts the B*H streams on its second dimension.
+bool streams_ok(int B, int H, const char* fn, int* status) {
+  if ((long long)B * H > 65535) {
+    *status = fail(PLX_EINVAL, "%s: B*H must not exceed 65535 (got %lld)", fn, (long long)B * H);
+    return false;
+  }
+  return true;
+}
+
+bool dtype_ok(int dtype, const char* fn, int* status) {
+  if (dtype != PLX_F32 && dtype != PLX_BF16) {
+    *status = fail(PLX_EUNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+    return false;
+  }
+  return true;
+}
+
+float eff_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / std::sqrt((float)d); }
+
+size_t vt_bytes(int B, int H, int L, int d) {
+  const size_t n_kt = (size_t)((L + kTileKeys - 1) / kTileKeys);
+  return (size_t)B * H * n_kt * kTileKeys * d * 2;
+}
+
+size_t part_bytes(int B, int H, int Lmax, int d, int C) {
+  const size_t S = (size_t)((Lmax + C - 1) / C);
+  return (size_t)B * H * S * (2 * d + 4) * sizeof(float);
+}
+
+int default_split(int B, int H, int Lmax) {
+  // aim at ~8k workgroups for the split pass (32 per CU); keep a split at
+  // least 256 keys so the partial records stay a small fraction of the traffic
+  long long target = 8192;
+  long long c = ((long long)Lmax * B * H + target - 1) / target;
+  int C = 256;
+  while (C < c && C < 16384) C <<= 1;
+  return C;
+}
+
+bool split_ok(int C, const char* fn, int* status) {
+  if (C <= 0 || C % kTileKeys != 0) {
+    *status = fail(PLX_EINVAL, "%s: split_keys must be a positive multiple of 64 (got %d)",
+                   fn, C);
+    return false;
+  }
+  return true;
+}
+
+// Stream-ordered scratch used when the caller passes no workspace.
+struct Scratch {
+  void* ptr = nullptr;
+  hipStream_t stream = nullptr;
+  ~Scratch() {
+    if (ptr) (void)hipFreeAsync(ptr, stream);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+int parallax_abi_version(void) { return PARALLAX_ABI_VERSION; }
+
+const char* parallax_last_error(void) { return g_err; }
+
+size_t parallax_prefill_workspace_bytes(int B, int H, int L, int d, int dtype) {
+  if (B <= 0 || H <= 0 || L <= 0 || (d != 64 && d != 128) || dtype != PLX_BF16) return 0;
+  return vt_bytes(B, H, L, d);
+}
+
+int parallax_prefill_stage_v(const void* v, void* vt16, int B, int H, int L, int d,
+                             void* stream) {
+  int st = PLX_OK;
+  if (!dims_ok(B, H, L, d, "parallax_prefill_stage_v", "L", &st)) return st;
+  if (!v || !vt16) return fail(PLX_EINVAL, "parallax_prefill_stage_v: null pointer");
+  hipError_t e = plx::launch_stage_v(v, vt16, B * H, L, d, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("parallax_prefill_stage_v launch", e);
+  return ok();
+}
+
+int parallax_prefill_attend(const void* q, const void* k, const void* vt16, const void* rho,
+                            const float* gate, float* out, int B, int H, int L, int d,
+                            float scale, void* stream) {
+  int st = PLX_OK;
+  if (!dims_ok(B, H, L, d, "parallax_prefill_attend", "L", &st)) return st;
+  if (!q || !k || !vt16 || !rho || !gate || !out)
+    return fail(PLX_EINVAL, "parallax_prefill_attend: null pointer");
+  hipError_t e = plx::launch_prefill_bf16(q, k, vt16, rho, gate, out, B, H, L, d,
+                                          eff_scale(scale, d), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("parallax_prefill_attend launch", e);
+  return ok();
+}
+
+int parallax_prefill(const void* q, const void* k, const void* v, const void* rho,
+                     const float* gate, float* out, int B, int H, int L, int d, float scale,
+                     int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "parallax_prefill";
+  int st = PLX_OK;
+  if (!dims_ok(B, H, L, d, fn, "L", &st)) return st;
+  if (!dtype_ok(dtype, fn, &st)) return st;
+  if (!q || !k || !v || !rho || !gate || !out) return fail(PLX_EINVAL, "%s: null pointer", fn);
+  hipStream_t s = (hipStream_t)stream;
+  const float sc = eff_scale(scale, d);
+  if (dtype == PLX_F32) {
+    hipError_t e = plx::launch_prefill_f32(q, k, v, rho, gate, out, B, H, L, d, sc, s);
+    if (e != hipSuccess) return hip_fail("parallax_prefill launch", e);
+    return ok();
+  }
+  const size_t need = vt_bytes(B, H, L, d);
+  Scratch scratch;
+  void* ws = workspace;
+  if (ws) {
+    if (workspace_bytes < need)
+      return fail(PLX_EINVAL, "%s: workspace of %zu bytes is smaller than the %zu required", fn,
+                  workspace_bytes, need);
+  } else {
+    hipError_t e = hipMallocAsync(&scratch.ptr, need, s);
+    if (e != hipSuccess) return fail(PLX_ENOMEM, "%s: hipMallocAsync(%zu): %s", fn, need,
+                                     hipGetErrorString(e));
+    scratch.stream = s;
+    ws = scratch.ptr;
+  }
+  hipError_t e = plx::launch_stage_v(v, ws, B * H, L, d, s);
+  if (e != hipSuccess) return hip_fail("parallax_prefill stage_v launch", e);
+  e = plx::launch_prefill_bf16(q, k, ws, rho, gate, out, B, H, L, d, sc, s);
+  if (e != hipSuccess) return hip_fail("parallax_prefill launch", e);
+  return ok();
+}
+
+int parallax_decode_default_split(int B, int H, int Lmax, int d) {
+  (void)d;
+  if (B <= 0 || H <= 0 || Lmax <= 0) return 0;
+  return default_split(B, H, Lmax);
+}
+
+size_t parallax_decode_workspace_bytes(int B, int H, int Lmax, int d, int split_keys) {
+  if (B <= 0 || H <= 0 || Lmax <= 0 || (d != 64 && d != 128)) return 0;
+  const int C = split_keys > 0 ? split_keys : default_split(B, H, Lmax);
+  if (C % kTileKeys) return 0;
+  return part_bytes(B, H, Lmax, d, C);
+}
+
+int parallax_decode_partials(const void* q, const void* kcache, const void* vcache,
+                             const void* rho, const int32_t* seqlens, float* partials, int B,
+                             int H, int Lmax, int d, float scale, int dtype, int split_keys,
+                             void* stream) {
+  const char* fn = "parallax_decode_partials";
+  int st = PLX_OK;
+  if (!dims_ok(B, H, Lmax, d, fn, "Lmax", &st)) return st;
+  if (!streams_ok(B, H, fn, &st)) return st;
+  if (!dtype_ok(dtype, fn, &st)) return st;
+  if (!split_ok(split_keys, fn, &st)) return st;
+  if (!q || !kcache || !vcache || !rho || !seqlens || !partials)
+    return fail(PLX_EINVAL, "%s: null pointer", fn);
+  hipError_t e = plx::launch_decode_split(q, kcache, vcache, rho, seqlens, partials, B, H, Lmax,
+                                          d, split_keys, eff_scale(scale, d),
+                                          dtype == PLX_BF16, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("parallax_decode_partials launch", e);
+  return ok();
+}
+
+int parallax_decode_combine(const float* partials, const float* gate, const int32_t* seqlens,
+                            float* out, int B, int H, int Lmax, int d, int split_keys,
+                            void* stream) {
+  const char* fn = "parallax_decode_combine";
+  int st = PLX_OK;
+  if (!dims_ok(B, H, Lmax, d, fn, "Lmax", &st)) return st;
+  if (!split_ok(split_keys, fn, &st)) return st;
+  if (!partials || !gate || !seqlens || !out) return fail(PLX_EINVAL, "%s: null pointer", fn);
+  hipError_t e = plx::launch_decode_combine(partials, gate, seqlens, out, B, H, Lmax, d,
+                                            split_keys, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("parallax_decode_combine launch", e);
+  return ok();
+}
+
+int parallax_decode(const void* q, const void* kcache, const void* vcache, const void* rho,
+                    const float* gate, float* out, const int32_t* seqlens, int B, int H,
+                    int Lmax, int d, float scale, int dtype, int split_keys, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  const char* fn = "parallax_decode";
+  int st = PLX_OK;
+  if (!dims_ok(B, H, Lmax, d, fn, "Lmax", &st)) return st;
+  if (!streams_ok(B, H, fn, &st)) return st;
+  if (!dtype_ok(dtype, fn, &st)) return st;
+  const int C = split_keys > 0 ? split_keys : default_split(B, H, Lmax);
+  if (split_keys < 0 || !split_ok(C, fn, &st))
+    return split_keys < 0 ? fail(PLX_EINVAL, "%s: split_keys must be >= 0", fn) : st;
+  if (!q || !kcache || !vcache || !rho || !gate || !out || !seqlens)
+    return fail(PLX_EINVAL, "%s: null pointer", fn);
+  hipStream_t s = (hipStream_t)stream;
+  const size_t need = part_bytes(B, H, Lmax, d, C);
+  Scratch scratch;
+  void* ws = workspace;
+  if (ws) {
+    if (workspace_bytes < need)
+      return fail(PLX_EINVAL, "%s: workspace of %zu bytes is smaller than the %zu required", fn,
+                  workspace_bytes, need);
+  } else {
+    hipError_t e = hipMallocAsync(&scratch.ptr, need, s);
+    if (e != hipSuccess) return fail(PLX_ENOMEM, "%s: hipMallocAsync(%zu): %s", fn, need,
+                                     hipGetErrorString(e));
+    scratch.stream = s;
+    ws = scratch.ptr;
+  }
+  float* part = static_cast<float*>(ws);
+  hipError_t e = plx::launch_decode_split(q, kcache, vcache, rho, seqlens, part, B, H, Lmax, d,
+                                          C, eff_scale(scale, d), dtype == PLX_BF16, s);
+  if (e != hipSuccess) return hip_fail("parallax_decode split launch", e);
+  e = plx::launch_decode_combine(part, gate, seqlens, out, B, H, Lmax, d, C, s);
+  if (e != hipSuccess) return hip_fail("parallax_decode combine launch", e);
+  return ok();
+}
+
+}  // extern "C"

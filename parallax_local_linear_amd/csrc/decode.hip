@@ -1,0 +1,263 @@
+// Split-KV Parallax decode on gfx950.
+//
+// One query per (b,h) attends every cached key of its sequence (page "Parallax -
+// Parameterized Local Linear Attention for Language Modeling", section "Core
+// mechanism", Eq. 2).  Both branches, softmax and covariance, consume the same
+// single pass over K and V (section "Hardware-aware algorithm"): the kernel is
+// bound by HBM bandwidth, so the design goal is one coalesced read of every
+// valid cache byte and nothing else.
+//
+// decode_split_kernel: grid (S, B*H), S = ceil(Lmax / C).  Workgroup s of a
+//   stream covers keys [s*C, min((s+1)*C, L_b)) and exits at once when that range
+//   is empty.  Inside a wave a key row is spread over LPR lanes, 16 bytes each,
+//   so one load instruction covers KPW consecutive rows of contiguous memory.
+//   Each lane keeps U row-loads of K and U of V in flight.  The partial dot
+//   products <q,k> and <rho,k> of a row are summed across its lanes with DPP;
+//   every lane group keeps its own online-softmax state (m, l, c) and the
+//   accumulators sum p v and sum p r v for its features.  At the end the
+//   groups of all four waves merge through LDS into one partial record.
+// decode_combine_kernel: one workgroup per (b,h) merges the records of its
+//   splits, rescaling by 2^(m_s - M), and applies the output formula.
+
+#include "plx_common.h"
+
+namespace plx {
+
+template <typename T, int D>
+struct DecCfg {
+  static constexpr int EPL = 16 / (int)sizeof(T);   // elements per lane per row load
+  static constexpr int LPR = D / EPL;                // lanes per key row
+  static constexpr int KPW = 64 / LPR;               // rows per wave load
+  static constexpr int U = 8;                        // row loads in flight per lane
+  static constexpr int CHUNK = KPW * U;              // keys per wave iteration
+  static constexpr int NG = 4 * KPW;                 // lane groups per workgroup
+};
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+template <typename T, int D>
+__global__ __launch_bounds__(256)
+void decode_split_kernel(const T* __restrict__ q, const T* __restrict__ kc,
+                         const T* __restrict__ vc, const T* __restrict__ rho,
+                         const int* __restrict__ seqlens, float* __restrict__ part,
+                         int H, int Lmax, int C, int S, float sl2) {
+  using CF = DecCfg<T, D>;
+  constexpr int EPL = CF::EPL, LPR = CF::LPR, KPW = CF::KPW, U = CF::U, NG = CF::NG;
+  __shared__ float s_m[NG], s_l[NG], s_c[NG];
+  __shared__ float s_a[NG][D], s_b[NG][D];
+
+  const int s = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / H;
+  const int Lb = min(max(seqlens[b], 0), Lmax);
+  const int k_begin = s * C;
+  if (k_begin >= Lb) return;                    // uniform over the workgroup
+  const int k_end = min(k_begin + C, Lb);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int grp = lane / LPR;
+  const int sub = lane % LPR;
+  const size_t head = (size_t)bh * Lmax * D;
+
+  // this lane's slice of q and rho: features sub*EPL .. +EPL-1
+  const u32x4 qw = *reinterpret_cast<const u32x4*>(q + (size_t)bh * D + sub * EPL);
+  const u32x4 rw = *reinterpret_cast<const u32x4*>(rho + (size_t)bh * D + sub * EPL);
+
+  float A[EPL], Bv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) { A[e] = 0.f; Bv[e] = 0.f; }
+  float m_run = kMinit, l_run = 0.f, c_run = 0.f;
+
+  const T* kb = kc + head + sub * EPL;
+  const T* vb = vc + head + sub * EPL;
+
+  for (int c0 = k_begin + wave * CF::CHUNK; c0 < k_end; c0 += 4 * CF::CHUNK) {
+    u32x4 kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = c0 + u * KPW + grp;
+      if (key < k_end) {
+        kr[u] = *reinterpret_cast<const u32x4*>(kb + (size_t)key * D);
+        vr[u] = *reinterpret_cast<const u32x4*>(vb + (size_t)key * D);
+      } else {
+        kr[u] = u32x4{0u, 0u, 0u, 0u};
+        vr[u] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    float sv[U], rv[U];
+    float mx = kMinit;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float sp = 0.f, rp = 0.f;
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          sp = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw[w]), as_bf16x2(kr[u][w]), sp, false);
+          rp = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(rw[w]), as_bf16x2(kr[u][w]), rp, false);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float kx = __uint_as_float(kr[u][w]);
+          sp = fmaf(__uint_as_float(qw[w]), kx, sp);
+          rp = fmaf(__uint_as_float(rw[w]), kx, rp);
+        }
+      }
+      sp = group_sum<LPR>(sp);
+      rp = group_sum<LPR>(rp);
+      const int key = c0 + u * KPW + grp;
+      sv[u] = (key < k_end) ? sp : -INFINITY;
+      rv[u] = rp;
+      mx = fmaxf(mx, sv[u]);
+    }
+    const float m_new = fmaxf(m_run, mx * sl2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+    c_run *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) { A[e] *= alpha; Bv[e] *= alpha; }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sv[u], sl2, -m_new));
+      const float t = p * rv[u];
+      l_run += p;
+      c_run += t;
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float v0 = bf16lo_to_f32(vr[u][w]);
+          const float v1 = bf16hi_to_f32(vr[u][w]);
+          A[2 * w] = fmaf(p, v0, A[2 * w]);
+          A[2 * w + 1] = fmaf(p, v1, A[2 * w + 1]);
+          Bv[2 * w] = fmaf(t, v0, Bv[2 * w]);
+          Bv[2 * w + 1] = fmaf(t, v1, Bv[2 * w + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float vx = __uint_as_float(vr[u][w]);
+          A[w] = fmaf(p, vx, A[w]);
+          Bv[w] = fmaf(t, vx, Bv[w]);
+        }
+      }
+    }
+  }
+
+  // merge the lane groups of all waves
+  const int gi = wave * KPW + grp;
+  if (sub == 0) {
+    s_m[gi] = m_run;
+    s_l[gi] = l_run;
+    s_c[gi] = c_run;
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    s_a[gi][sub * EPL + e] = A[e];
+    s_b[gi][sub * EPL + e] = Bv[e];
+  }
+  __syncthreads();
+  float M = kMinit;
+#pragma unroll
+  for (int i = 0; i < NG; ++i) M = fmaxf(M, s_m[i]);
+  float* rec = part + ((size_t)bh * S + s) * (2 * D + 4);
+  for (int t = tid; t < 2 * D; t += 256) {
+    const int f = t % D;
+    float acc = 0.f;
+    if (t < D) {
+#pragma unroll
+      for (int i = 0; i < NG; ++i) acc += __builtin_amdgcn_exp2f(s_m[i] - M) * s_a[i][f];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NG; ++i) acc += __builtin_amdgcn_exp2f(s_m[i] - M) * s_b[i][f];
+    }
+    rec[4 + t] = acc;
+  }
+  if (tid == 0) {
+    float lt = 0.f, ct = 0.f;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const float w = __builtin_amdgcn_exp2f(s_m[i] - M);
+      lt += w * s_l[i];
+      ct += w * s_c[i];
+    }
+    rec[0] = M;
+    rec[1] = lt;
+    rec[2] = ct;
+    rec[3] = 0.f;
+  }
+}
+
+// Merge the split records of one (b,h) and write o = o_sa - g (u - o_sa rbar).
+template <int D>
+__global__ __launch_bounds__(D)
+void decode_combine_kernel(const float* __restrict__ part, const float* __restrict__ gate,
+                           const int* __restrict__ seqlens, float* __restrict__ out,
+                           int H, int Lmax, int C, int S) {
+  const int bh = blockIdx.x;
+  const int b = bh / H, h = bh % H;
+  const int f = threadIdx.x;
+  const int Lb = min(max(seqlens[b], 0), Lmax);
+  const int ns = (Lb + C - 1) / C;
+  float* o = out + (size_t)bh * D;
+  if (ns == 0) {
+    o[f] = 0.f;
+    return;
+  }
+  const float* rec = part + (size_t)bh * S * (2 * D + 4);
+  float M = kMinit;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, rec[(size_t)s * (2 * D + 4)]);
+  float l = 0.f, c = 0.f, a = 0.f, bv = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float* r = rec + (size_t)s * (2 * D + 4);
+    const float w = __builtin_amdgcn_exp2f(r[0] - M);
+    l += w * r[1];
+    c += w * r[2];
+    a += w * r[4 + f];
+    bv += w * r[4 + D + f];
+  }
+  const float inv = 1.0f / l;
+  const float osa = a * inv;
+  const float uu = bv * inv;
+  o[f] = osa - gate[h] * (uu - osa * (c * inv));
+}
+
+template <typename T, int D>
+static hipError_t launch_split_t(const void* q, const void* kc, const void* vc,
+                                 const void* rho, const int* seqlens, float* part, int B,
+                                 int H, int Lmax, int C, float sl2, hipStream_t s) {
+  const int S = (Lmax + C - 1) / C;
+  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3((unsigned)S, (unsigned)(B * H)),
+                     dim3(256), 0, s, (const T*)q, (const T*)kc, (const T*)vc,
+                     (const T*)rho, seqlens, part, H, Lmax, C, S, sl2);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_split(const void* q, const void* kc, const void* vc, const void* rho,
+                               const int* seqlens, float* part, int B, int H, int Lmax, int d,
+                               int C, float scale, bool bf16, hipStream_t s) {
+  const float sl2 = scale * kLog2e;
+  if (bf16) {
+    if (d == 128) return launch_split_t<__bf16, 128>(q, kc, vc, rho, seqlens, part, B, H, Lmax, C, sl2, s);
+    return launch_split_t<__bf16, 64>(q, kc, vc, rho, seqlens, part, B, H, Lmax, C, sl2, s);
+  }
+  if (d == 128) return launch_split_t<float, 128>(q, kc, vc, rho, seqlens, part, B, H, Lmax, C, sl2, s);
+  return launch_split_t<float, 64>(q, kc, vc, rho, seqlens, part, B, H, Lmax, C, sl2, s);
+}
+
+hipError_t launch_decode_combine(const float* part, const float* gate, const int* seqlens,
+                                 float* out, int B, int H, int Lmax, int d, int C,
+                                 hipStream_t s) {
+  const int S = (Lmax + C - 1) / C;
+  if (d == 128)
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((unsigned)(B * H)), dim3(128), 0, s,
+                       part, gate, seqlens, out, H, Lmax, C, S);
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((unsigned)(B * H)), dim3(64), 0, s,
+                       part, gate, seqlens, out, H, Lmax, C, S);
+  return hipGetLastError();
+}
+
+}  // namespace plx

@@ -1,0 +1,322 @@
+// Causal Parallax prefill in bf16 on CDNA4 matrix cores (gfx950).
+//
+// Computes, for every query i of every (b,h) head (page "Parallax - Parameterized
+// Local Linear Attention for Language Modeling", section "Core mechanism", Eq. 2):
+//     o_i = o^SA_i - g_h ( sum_j w_ij r_ij v_j - o^SA_i sum_j w_ij r_ij ),   j <= i
+// with w_ij the causal softmax weights of scale <q_i,k_j> and r_ij = <rho_i,k_j>,
+// in one streaming pass over the keys shared by both branches (section
+// "Hardware-aware algorithm").
+//
+// Work decomposition
+//   * A workgroup owns 128 consecutive queries of one head (4 waves x 32 rows)
+//     and walks the causal key range in tiles of 64 keys.  Every K tile (bf16)
+//     and V^T tile (fp16, pre-staged by stage_v) is copied from HBM to LDS once
+//     per workgroup, double-buffered through registers, and read by all waves.
+//   * Each wave computes the transposed score tiles S^T = K Q^T and R^T = K rho^T
+//     with v_mfma_f32_32x32x16_bf16.  One K fragment read from LDS feeds both
+//     MFMAs (the joint QK / RK product).  Q and rho fragments stay in registers.
+//   * In the transposed layout a lane owns one query and 16 keys per 32-key
+//     block, so the online-softmax row reductions are lane-local except for one
+//     exchange with the lane 32 apart.
+//   * P = exp2(S*scale*log2e - m) and T = P*R are rounded to fp16 (RNE) and fed,
+//     as B operands, to v_mfma_f32_32x32x16_f16 against the V^T fragment:
+//     O^T += V^T P^T and A_r^T += V^T T^T, fp32 accumulators in registers.  The
+//     row sums l = sum P and c = sum T are taken from the same rounded values
+//     (v_dot2_f32_f16 against (1,1)), so a single key reproduces v exactly.
+//   * K rows are read into the A operand in a permuted order (bits 2 and 3 of the
+//     row swapped) so that the score accumulators of a lane line up, 8 at a
+//     time, with 8 consecutive keys of the V^T tile: P and T go from the score
+//     MFMA output straight into the value MFMA input without any data movement.
+//   * Grid order: the longest (last) query tiles of every head first; heads
+//     cycle fastest so that the 8 XCDs each receive a fixed subset of heads.
+
+#include "plx_common.h"
+
+namespace plx {
+
+constexpr int PF_BR = 128;      // queries per workgroup
+constexpr int PF_BC = 64;       // keys per tile
+constexpr int PF_THREADS = 256;
+
+template <int D>
+struct PfLayout {
+  static constexpr int KS = D + 8;          // LDS row pitch of a K tile (bf16 elements)
+  static constexpr int VS = PF_BC + 8;      // LDS row pitch of a V^T tile (fp16 elements)
+  static constexpr int K_ELEMS = PF_BC * KS;
+  static constexpr int V_ELEMS = D * VS;
+  static constexpr int STAGE = K_ELEMS + V_ELEMS;   // 2-byte elements per buffer
+};
+
+template <int D>
+__global__ __launch_bounds__(PF_THREADS, 1)
+void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                         const _Float16* __restrict__ vt, const __bf16* __restrict__ rho,
+                         const float* __restrict__ gate, float* __restrict__ out,
+                         int H, int L, int BH, int n_qt, float sl2) {
+  using LY = PfLayout<D>;
+  constexpr int KSTEPS = D / 16;                         // MFMA steps over features
+  constexpr int DB = D / 32;                             // 32-feature output blocks
+  constexpr int KCH = PF_BC * D / 8 / PF_THREADS;        // 16-B K chunks / thread / tile
+  constexpr int VCH = D * PF_BC / 8 / PF_THREADS;        // 16-B V^T chunks / thread / tile
+  constexpr int KROW_CH = D / 8;                         // 16-B chunks per K row
+
+  __shared__ __align__(16) uint16_t smem[2 * LY::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  const int qt = n_qt - 1 - (int)(blockIdx.x / (unsigned)BH);
+  const int bh = (int)(blockIdx.x % (unsigned)BH);
+  const int h = bh % H;
+  const int q0 = qt * PF_BR;
+  const int qw0 = q0 + wave * 32;
+  const int qi = qw0 + l32;
+  const size_t head = (size_t)bh * L * D;
+  const int n_kt_all = (L + PF_BC - 1) / PF_BC;
+
+  // B-operand fragments: query qi, features 16*kk + 8*g .. +7
+  bf16x8 qf[KSTEPS], rf[KSTEPS];
+  if (qi < L) {
+    const bf16x8* qp = reinterpret_cast<const bf16x8*>(q + head + (size_t)qi * D);
+    const bf16x8* rp = reinterpret_cast<const bf16x8*>(rho + head + (size_t)qi * D);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      qf[kk] = qp[2 * kk + g];
+      rf[kk] = rp[2 * kk + g];
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      qf[kk] = bf16x8{};
+      rf[kk] = bf16x8{};
+    }
+  }
+
+  f32x16 acc_o[DB], acc_r[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    acc_o[db] = f32x16{};
+    acc_r[db] = f32x16{};
+  }
+  float m_run = kMinit, l_run = 0.f, c_run = 0.f;
+
+  const int last_q = min(q0 + PF_BR, L) - 1;
+  const int n_kt = last_q / PF_BC + 1;
+  const int wave_last_q = min(qw0 + 31, L - 1);
+
+  u32x4 kreg[KCH], vreg[VCH];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+      const int ch = tid + c * PF_THREADS;
+      const int key = kt * PF_BC + ch / KROW_CH;
+      kreg[c] = (key < L)
+          ? *reinterpret_cast<const u32x4*>(k + head + (size_t)key * D + (ch % KROW_CH) * 8)
+          : u32x4{0u, 0u, 0u, 0u};
+    }
+    const _Float16* vtile = vt + ((size_t)bh * n_kt_all + kt) * (size_t)(D * PF_BC);
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      const int ch = tid + c * PF_THREADS;
+      vreg[c] = *reinterpret_cast<const u32x4*>(vtile + (size_t)ch * 8);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t* ks = smem + buf * LY::STAGE;
+    uint16_t* vs = ks + LY::K_ELEMS;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+      const int ch = tid + c * PF_THREADS;
+      *reinterpret_cast<u32x4*>(ks + (ch / KROW_CH) * LY::KS + (ch % KROW_CH) * 8) = kreg[c];
+    }
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      const int ch = tid + c * PF_THREADS;
+      *reinterpret_cast<u32x4*>(vs + (ch / (PF_BC / 8)) * LY::VS + (ch % (PF_BC / 8)) * 8) =
+          vreg[c];
+    }
+  };
+
+  // A-operand row of this lane inside a 32-key block: bits 2 and 3 swapped
+  const int prow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_kt) load_tile(kt + 1);
+    const int k0 = kt * PF_BC;
+    if (qw0 < L && k0 <= wave_last_q) {
+      const uint16_t* ks = smem + buf * LY::STAGE;
+      const uint16_t* vs = ks + LY::K_ELEMS;
+      const bool diag = (k0 + PF_BC - 1 > qw0);
+
+      f32x16 sacc[2], racc[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        sacc[b] = f32x16{};
+        racc[b] = f32x16{};
+        const uint16_t* krow = ks + (32 * b + prow) * LY::KS + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * kk);
+          sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[b], 0, 0, 0);
+          racc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, rf[kk], racc[b], 0, 0, 0);
+        }
+      }
+
+      // causal mask (diagonal tiles only) and the row maximum
+      float mx = kMinit;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (diag) {
+            const int key = k0 + 32 * b + 16 * (e >> 3) + 8 * g + (e & 7);
+            if (key > qi) sacc[b][e] = -INFINITY;
+          }
+          mx = fmaxf(mx, sacc[b][e]);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * sl2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      c_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        acc_o[db] *= alpha;
+        acc_r[db] *= alpha;
+      }
+
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          f16x8 pf, tf;
+#pragma unroll
+          for (int e8 = 0; e8 < 8; ++e8) {
+            const int e = 8 * u + e8;
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][e], sl2, -m_new));
+            const float t = p * racc[b][e];
+            pf[e8] = (_Float16)p;
+            tf[e8] = (_Float16)t;
+          }
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const f16x2 pp = {pf[2 * e2], pf[2 * e2 + 1]};
+            const f16x2 tt = {tf[2 * e2], tf[2 * e2 + 1]};
+            l_run = __builtin_amdgcn_fdot2(pp, ones, l_run, false);
+            c_run = __builtin_amdgcn_fdot2(tt, ones, c_run, false);
+          }
+          const uint16_t* vrow = vs + l32 * LY::VS + 16 * (2 * b + u) + 8 * g;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const f16x8 va = *reinterpret_cast<const f16x8*>(vrow + 32 * db * LY::VS);
+            acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf, acc_o[db], 0, 0, 0);
+            acc_r[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, tf, acc_r[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (kt + 1 < n_kt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: o = o_sa - g (u - o_sa * rbar), o_sa = O/l, u = A_r/l, rbar = c/l
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float c_tot = c_run + __shfl_xor(c_run, 32);
+  if (qi < L) {
+    const float inv = 1.0f / l_tot;
+    const float rbar = c_tot * inv;
+    const float gh = gate[h];
+    float* orow = out + head + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 o;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float osa = acc_o[db][4 * i + jj] * inv;
+          const float uu = acc_r[db][4 * i + jj] * inv;
+          o[jj] = osa - gh * (uu - osa * rbar);
+        }
+        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * i + 4 * g) = o;
+      }
+    }
+  }
+}
+
+// V [BH, L, D] bf16 -> V^T tiles [BH][ceil(L/64)][D][64] fp16, zero past L.
+// One workgroup per (head, 64-key tile): coalesced 16-B loads into LDS, then
+// each thread gathers 8 keys of one feature, converts and stores 16 B.
+template <int D>
+__global__ __launch_bounds__(256)
+void stage_v_kernel(const __bf16* __restrict__ v, _Float16* __restrict__ vt, int L, int n_kt) {
+  constexpr int PITCH = D + 2;     // odd dword pitch spreads the column reads over banks
+  __shared__ uint16_t tile[PF_BC * PITCH];
+  const int bh = blockIdx.x / n_kt;
+  const int kt = blockIdx.x % n_kt;
+  const int tid = threadIdx.x;
+  const __bf16* src = v + ((size_t)bh * L + (size_t)kt * PF_BC) * D;
+  constexpr int CH = PF_BC * D / 8;
+  for (int ch = tid; ch < CH; ch += 256) {
+    const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (kt * PF_BC + row < L) w = *reinterpret_cast<const u32x4*>(src + (size_t)row * D + col);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(tile + row * PITCH + col);
+    dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2]; dst[3] = w[3];
+  }
+  __syncthreads();
+  _Float16* dst = vt + ((size_t)bh * n_kt + kt) * (size_t)(D * PF_BC);
+  for (int ch = tid; ch < CH; ch += 256) {
+    const int f = ch / (PF_BC / 8), key0 = (ch % (PF_BC / 8)) * 8;
+    f16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = __uint_as_float((uint32_t)tile[(key0 + e) * PITCH + f] << 16);
+      o[e] = (_Float16)x;
+    }
+    *reinterpret_cast<f16x8*>(dst + (size_t)ch * 8) = o;
+  }
+}
+
+hipError_t launch_stage_v(const void* v, void* vt, int BH, int L, int d, hipStream_t s) {
+  const int n_kt = (L + PF_BC - 1) / PF_BC;
+  const dim3 grid((unsigned)(BH * n_kt));
+  if (d == 128)
+    hipLaunchKernelGGL(stage_v_kernel<128>, grid, dim3(256), 0, s, (const __bf16*)v,
+                       (_Float16*)vt, L, n_kt);
+  else
+    hipLaunchKernelGGL(stage_v_kernel<64>, grid, dim3(256), 0, s, (const __bf16*)v,
+                       (_Float16*)vt, L, n_kt);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_bf16(const void* q, const void* k, const void* vt, const void* rho,
+                               const float* gate, float* out, int B, int H, int L, int d,
+                               float scale, hipStream_t s) {
+  const int BH = B * H;
+  const int n_qt = (L + PF_BR - 1) / PF_BR;
+  const dim3 grid((unsigned)(BH * n_qt));
+  const float sl2 = scale * kLog2e;
+  if (d == 128)
+    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(PF_THREADS), 0, s,
+                       (const __bf16*)q, (const __bf16*)k, (const _Float16*)vt,
+                       (const __bf16*)rho, gate, out, H, L, BH, n_qt, sl2);
+  else
+    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(PF_THREADS), 0, s,
+                       (const __bf16*)q, (const __bf16*)k, (const _Float16*)vt,
+                       (const __bf16*)rho, gate, out, H, L, BH, n_qt, sl2);
+  return hipGetLastError();
+}
+
+}  // namespace plx

@@ -1,0 +1,163 @@
+"""GPU parity of the prefill path against the fp64 CPU oracle.
+
+Tolerances (max-abs over every compared element): 1e-4 for fp32 inputs and
+2e-2 for bf16 inputs with fp32 accumulation; outputs are fp32.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import parallax_oracle as po
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _plx():
+    import parallax_local_linear_amd as plx
+    return plx
+
+
+def _host(x):
+    return x.detach().cpu()
+
+
+def _run(inp):
+    plx = _plx()
+    out = plx.prefill(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"])
+    torch.cuda.synchronize()
+    return _host(out).double().numpy()
+
+
+def _oracle_all(inp):
+    h = {k: _host(v) for k, v in inp.items()}
+    return po.prefill(h["q"], h["k"], h["v"], h["rho"], h["gate"])
+
+
+def _maxerr(a, b):
+    return float(np.max(np.abs(a - b)))
+
+
+def test_native_library_is_loaded():
+    plx = _plx()
+    import parallax_local_linear_amd._native as nat
+    assert plx.lib()._name == nat.LIB_PATH
+
+
+def test_workload1_fp32_full():
+    inp = wl.make_workload(1, device="cuda")
+    out = _run(inp)
+    ref = _oracle_all(inp)
+    err = _maxerr(out, ref)
+    print(f"workload 1 fp32 max-abs {err:.3e}", flush=True)
+    assert err <= TOL["f32"]
+    h = {k: _host(v) for k, v in inp.items()}
+    ex = po.prefill_explicit(h["q"], h["k"], h["v"], h["rho"], h["gate"])
+    assert _maxerr(out, ex) <= TOL["f32"]
+
+
+SHAPES = [(1, 1, 1), (1, 1, 2), (1, 2, 63), (1, 1, 64), (2, 1, 65), (1, 1, 127),
+          (1, 1, 128), (1, 2, 129), (1, 1, 255), (2, 2, 1000)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,L", SHAPES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_shapes(dtype, B, H, L, d):
+    inp = wl.prefill_inputs(B, H, L, d, dtype, seed=100 + L + d, device="cuda", rho_std=0.5,
+                            gate=("uniform", 0.2, 1.0))
+    out = _run(inp)
+    ref = _oracle_all(inp)
+    err = _maxerr(out, ref)
+    print(f"prefill {dtype} B{B} H{H} L{L} d{d}: max-abs {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_first_row_is_v0_exactly(dtype):
+    """A query that attends one key returns that key's value exactly."""
+    inp = wl.prefill_inputs(2, 3, 130, 128, dtype, seed=7, device="cuda", rho_std=2.0)
+    out = _plx().prefill(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"])
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, :, 0].cpu(), inp["v"][:, :, 0].float().cpu())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rho_zero_is_softmax_attention(dtype):
+    inp = wl.prefill_inputs(1, 2, 300, 64, dtype, seed=8, device="cuda")
+    inp["rho"].zero_()
+    out = _run(inp)
+    h = {k: _host(v).double() for k, v in inp.items()}
+    ref = torch.nn.functional.scaled_dot_product_attention(h["q"], h["k"], h["v"],
+                                                           is_causal=True).numpy()
+    assert _maxerr(out, ref) <= TOL[dtype] / 4
+
+
+def test_identical_keys_give_uniform_average():
+    inp = wl.prefill_inputs(1, 1, 200, 128, "bf16", seed=9, device="cuda", rho_std=1.0)
+    inp["k"].copy_(inp["k"][:, :, :1].expand_as(inp["k"]))
+    out = _run(inp)
+    v = _host(inp["v"]).double().numpy()
+    ref = np.cumsum(v, axis=2) / np.arange(1, 201)[None, None, :, None]
+    assert _maxerr(out, ref) <= TOL["bf16"]
+
+
+def test_deterministic():
+    inp = wl.prefill_inputs(1, 4, 700, 128, "bf16", seed=10, device="cuda")
+    plx = _plx()
+    a = plx.prefill(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"]).clone()
+    b = plx.prefill(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_stages_match_single_call():
+    plx = _plx()
+    inp = wl.prefill_inputs(2, 2, 333, 64, "bf16", seed=11, device="cuda")
+    a = plx.prefill(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"])
+    vt = plx.prefill_stage_v(inp["v"])
+    b = plx.prefill_attend(inp["q"], inp["k"], vt, inp["rho"], inp["gate"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def _sample_rows(L, rng, n_rand=24):
+    rows = {0, 1, 2, 3, L - 1}
+    rows.update(int(x) for x in rng.integers(0, L, n_rand))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("wid", [2, 5])
+def test_full_workload_sampled(wid):
+    """The full-size bf16 workloads, in the launch configuration the benchmark
+    times: every row of two heads by the expanded form, and sampled rows of
+    further heads by the explicit covariance form."""
+    w = wl.WORKLOADS[wid]
+    inp = wl.make_workload(wid, device="cuda")
+    plx = _plx()
+    out = plx.prefill(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    rng = np.random.default_rng(wid)
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    worst = 0.0
+    for b, h in heads:
+        hq = {k: _host(inp[k][b, h]).double().numpy() for k in ("q", "k", "v", "rho")}
+        g = float(inp["gate"][h])
+        ref = po.prefill_head(hq["q"], hq["k"], hq["v"], hq["rho"], g, w.scale)
+        err = _maxerr(_host(out[b, h]).double().numpy(), ref)
+        worst = max(worst, err)
+        print(f"workload {wid} head ({b},{h}) all rows: max-abs {err:.3e}", flush=True)
+    hcpu = {k: _host(inp[k]) for k in ("q", "k", "v", "rho", "gate")}
+    for _ in range(6):
+        b, h = int(rng.integers(0, w.B)), int(rng.integers(0, w.H))
+        rows = _sample_rows(w.L, rng)
+        ref = po.prefill_rows(hcpu["q"], hcpu["k"], hcpu["v"], hcpu["rho"], hcpu["gate"], b, h,
+                              rows, scale=w.scale)
+        got = _host(out[b, h, rows]).double().numpy()
+        err = _maxerr(got, ref)
+        worst = max(worst, err)
+    print(f"workload {wid}: worst max-abs {worst:.3e}", flush=True)
+    assert worst <= TOL["bf16"]
