@@ -1,0 +1,329 @@
+"""Benchmark of the Parallax forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+
+One step is one pass of the whole hot path over resident synthetic inputs:
+  1. bf16 causal prefill, B=4 H=16 L=4096 d=128 (V staging + fused kernel);
+  2. bf16 decode, B=64 H=16 d=128, 8192 cached keys per sequence
+     (split-KV partials + combine).
+Every launch is bracketed by HIP events on the stream it runs on (torch's
+current stream, which the library is handed).  `value` is the prefill
+throughput in TFLOP/s (algorithmic flops 8*d*B*H*L(L+1)/2 over the time of both
+prefill kernels); the decode throughput in GB/s (algorithmic bytes: K and V
+over the valid lengths plus q, rho, out, gate, seqlens) is reported beside it.
+`roofline` describes the dominant kernel (the fused prefill kernel), and the
+decode block carries its own for the split-KV kernel.
+
+Unless --no-extra is given, the two other full-size workloads (long ragged
+decode and the d=64 prefill) are timed too and reported under "extra".
+The CPU baseline times the fp64 oracle on a bounded sample on the host.
+Prints exactly one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("Parallax decode HBM GB/s (% of peak) + prefill TFLOP/s (% bf16 MFMA peak)")
+PEAK_MFMA_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, published
+PEAK_HBM_GBS = 8000.0               # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "prefill_bf16_kernel": "parallax_local_linear_amd/csrc/prefill_bf16.hip",
+    "decode_split_kernel": "parallax_local_linear_amd/csrc/decode.hip",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_sha(kernel):
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic(kernel):
+    """HBM bytes per launch measured with rocprofv3 counters for this exact
+    kernel source, or None when no measurement matches the current source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("src_sha") != src_sha(kernel):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """Per-label lists of HIP-event pairs recorded on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.ev = {}
+
+    def run(self, label, fn):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.ev.setdefault(label, []).append((a, b))
+
+    def ms(self, label, skip=0):
+        pairs = self.ev[label][skip:]
+        return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+
+    def reset(self):
+        self.ev = {}
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return os.cpu_count()
+
+
+def cpu_baseline_prefill(inp, w, budget_s=12.0):
+    """fp64 oracle (expanded form) on whole heads of the prefill workload until
+    the time budget is spent; TFLOP/s over the same algorithmic count."""
+    from oracle import parallax_oracle as po
+    import workloads as wl
+    heads = 0
+    t_tot = 0.0
+    for idx in range(w.B * w.H):
+        b, h = divmod(idx, w.H)
+        arrs = {k: inp[k][b, h].float().cpu().double().numpy() for k in ("q", "k", "v", "rho")}
+        g = float(inp["gate"][h])
+        t0 = time.perf_counter()
+        po.prefill_head(arrs["q"], arrs["k"], arrs["v"], arrs["rho"], g, w.scale)
+        t_tot += time.perf_counter() - t0
+        heads += 1
+        if t_tot >= budget_s:
+            break
+    flops = wl.prefill_flops(1, heads, w.L, w.d)
+    return {"value": flops / t_tot / 1e12, "unit": "TFLOP/s", "cores": cpu_threads(),
+            "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads of the B{w.B} H{w.H} L{w.L} d{w.d} "
+                      f"prefill, fp64 expanded form, {t_tot:.1f}s"}
+
+
+def cpu_baseline_decode(inp, w, budget_s=6.0):
+    """fp64 oracle on whole decode streams until the time budget is spent."""
+    from oracle import parallax_oracle as po
+    H, d = w.H, w.d
+    n_streams, nbytes, t_tot = 0, 0, 0.0
+    sl = inp["seqlens"].cpu().tolist()
+    for idx in range(w.B * H):
+        b, h = divmod(idx, H)
+        n = sl[b]
+        K = inp["kcache"][b, h, :n].float().cpu().double().numpy()
+        V = inp["vcache"][b, h, :n].float().cpu().double().numpy()
+        q = inp["q"][b, h].float().cpu().double().numpy()
+        r = inp["rho"][b, h].float().cpu().double().numpy()
+        t0 = time.perf_counter()
+        po.decode_stream(q, K, V, r, float(inp["gate"][h]), w.scale)
+        t_tot += time.perf_counter() - t0
+        n_streams += 1
+        nbytes += n * 2 * d * 2 + 2 * d * 2 + d * 4
+        if t_tot >= budget_s:
+            break
+    return {"value": nbytes / t_tot / 1e9, "unit": "GB/s", "cores": cpu_threads(),
+            "kind": "oracle",
+            "sample": f"{n_streams} of {w.B * H} streams of the decode workload, fp64, "
+                      f"bytes counted as bf16, {t_tot:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true", help="skip workloads 4 and 5")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (a "
+                         "known-size kernel for scaling HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import parallax_local_linear_amd as plx
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wp, wd = wl.WORKLOADS[2], wl.WORKLOADS[3]
+    log("generating inputs")
+    pin = wl.make_workload(2, device=dev)
+    din = wl.make_workload(3, device=dev)
+    B, H, L, d = wp.B, wp.H, wp.L, wp.d
+    vt = torch.empty(plx.prefill_workspace_bytes(B, H, L, d), dtype=torch.uint8, device=dev)
+    pout = torch.empty((B, H, L, d), dtype=torch.float32, device=dev)
+    C = plx.decode_default_split(wd.B, wd.H, wd.Lmax, wd.d)
+    S = -(-wd.Lmax // C)
+    part = torch.empty((wd.B, wd.H, S, 2 * wd.d + 4), dtype=torch.float32, device=dev)
+    dout = torch.empty((wd.B, wd.H, wd.d), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    tm = Timer(torch)
+
+    def step():
+        tm.run("stage_v", lambda: plx.prefill_stage_v(pin["v"], vt))
+        tm.run("attend", lambda: plx.prefill_attend(pin["q"], pin["k"], vt, pin["rho"],
+                                                    pin["gate"], out=pout))
+        tm.run("partials", lambda: plx.decode_partials(din["q"], din["kcache"], din["vcache"],
+                                                       din["rho"], din["seqlens"], C,
+                                                       partials=part))
+        tm.run("combine", lambda: plx.decode_combine(part, din["gate"], din["seqlens"],
+                                                     wd.Lmax, C, out=dout))
+
+    log("warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tm.reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms = {k: tm.ms(k) for k in ("stage_v", "attend", "partials", "combine")}
+    ms_step = wall * 1e3 / args.steps
+    flops = wl.prefill_flops(B, H, L, d)
+    pre_ms = ms["stage_v"] + ms["attend"]
+    value = flops / (pre_ms * 1e-3) / 1e12
+    att_tf = flops / (ms["attend"] * 1e-3) / 1e12
+    t_att = traffic("prefill_bf16_kernel")
+    dbytes = wl.decode_bytes(din["seqlens"].tolist(), wd.H, wd.d)
+    dec_ms = ms["partials"] + ms["combine"]
+    part_gbs = dbytes / (ms["partials"] * 1e-3) / 1e9
+    t_dec = traffic("decode_split_kernel")
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wp.name, "B": B, "H": H, "L": L, "d": d, "causal": True,
+                   "step": "prefill(B4 H16 L4096 d128) + decode(B64 H16 Lkv8192 d128)"},
+        "prefill": {"ms": round(pre_ms, 4), "tflops": round(value, 2),
+                    "frac_of_peak": round(value / PEAK_MFMA_BF16_TFLOPS, 4),
+                    "kernels_ms": {"stage_v": round(ms["stage_v"], 4),
+                                   "attend": round(ms["attend"], 4)},
+                    "flops": flops},
+        "roofline": {"kernel": "prefill_bf16_kernel<128>", "bound": "mfma",
+                     "achieved": round(att_tf, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(att_tf / PEAK_MFMA_BF16_TFLOPS, 4),
+                     "traffic": t_att},
+        "decode": {"workload": wd.name, "ms": round(dec_ms, 4),
+                   "value": round(dbytes / (dec_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                   "frac_of_peak": round(dbytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                   "split_keys": C, "bytes": dbytes,
+                   "kernels_ms": {"partials": round(ms["partials"], 4),
+                                  "combine": round(ms["combine"], 4)},
+                   "roofline": {"kernel": "decode_split_kernel<bf16,128>", "bound": "hbm",
+                                "achieved": round(part_gbs, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(part_gbs / PEAK_HBM_GBS, 4),
+                                "traffic": t_dec}},
+    }
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["calib_copy_bytes"] = {"read": n * 4, "write": n * 4}
+        del src, dst
+
+    if not args.no_extra:
+        res["extra"] = extra_workloads(torch, plx, wl, dev)
+
+    if not args.no_cpu:
+        log("cpu baseline")
+        res["cpu_baseline"] = cpu_baseline_prefill(pin, wp)
+        res["decode"]["cpu_baseline"] = cpu_baseline_decode(din, wd)
+    print(json.dumps(res), flush=True)
+
+
+def extra_workloads(torch, plx, wl, dev, steps=10):
+    """Long ragged decode (B8 H16, 65536..131072 keys) and the d=64 prefill."""
+    out = []
+    w4 = wl.WORKLOADS[4]
+    log("extra: decode workload 4")
+    din = wl.make_workload(4, device=dev)
+    C = plx.decode_default_split(w4.B, w4.H, w4.Lmax, w4.d)
+    S = -(-w4.Lmax // C)
+    part = torch.empty((w4.B, w4.H, S, 2 * w4.d + 4), dtype=torch.float32, device=dev)
+    dout = torch.empty((w4.B, w4.H, w4.d), dtype=torch.float32, device=dev)
+    tm = Timer(torch)
+    for i in range(steps + 2):
+        tm.run("partials", lambda: plx.decode_partials(din["q"], din["kcache"], din["vcache"],
+                                                       din["rho"], din["seqlens"], C,
+                                                       partials=part))
+        tm.run("combine", lambda: plx.decode_combine(part, din["gate"], din["seqlens"],
+                                                     w4.Lmax, C, out=dout))
+    torch.cuda.synchronize()
+    nb = wl.decode_bytes(din["seqlens"].tolist(), w4.H, w4.d)
+    ms = tm.ms("partials", 2) + tm.ms("combine", 2)
+    out.append({"workload": w4.name, "ms": round(ms, 4), "GB/s": round(nb / ms / 1e6, 1),
+                "frac_of_hbm_peak": round(nb / ms / 1e6 / PEAK_HBM_GBS, 4), "bytes": nb,
+                "seqlens": din["seqlens"].tolist(), "split_keys": C})
+    del din, part, dout
+    torch.cuda.empty_cache()
+
+    w5 = wl.WORKLOADS[5]
+    log("extra: prefill workload 5")
+    pin = wl.make_workload(5, device=dev)
+    vt = torch.empty(plx.prefill_workspace_bytes(w5.B, w5.H, w5.L, w5.d), dtype=torch.uint8,
+                     device=dev)
+    pout = torch.empty((w5.B, w5.H, w5.L, w5.d), dtype=torch.float32, device=dev)
+    tm = Timer(torch)
+    for i in range(steps + 2):
+        tm.run("stage_v", lambda: plx.prefill_stage_v(pin["v"], vt))
+        tm.run("attend", lambda: plx.prefill_attend(pin["q"], pin["k"], vt, pin["rho"],
+                                                    pin["gate"], out=pout))
+    torch.cuda.synchronize()
+    fl = wl.prefill_flops(w5.B, w5.H, w5.L, w5.d)
+    ms_a = tm.ms("attend", 2)
+    ms = tm.ms("stage_v", 2) + ms_a
+    out.append({"workload": w5.name, "ms": round(ms, 4),
+                "TFLOP/s": round(fl / ms / 1e9, 2),
+                "frac_of_mfma_peak": round(fl / ms / 1e9 / PEAK_MFMA_BF16_TFLOPS, 4),
+                "attend_ms": round(ms_a, 4),
+                "attend_TFLOP/s": round(fl / ms_a / 1e9, 2), "flops": fl})
+    del pin, vt, pout
+    torch.cuda.empty_cache()
+    return out
+
+
+if __name__ == "__main__":
+    main()
