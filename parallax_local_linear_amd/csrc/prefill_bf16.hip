@@ -8,25 +8,31 @@
 // "Hardware-aware algorithm").
 //
 // Work decomposition
-//   * A workgroup owns 128 consecutive queries of one head (4 waves x 32 rows)
+//   * A workgroup owns 16*NW consecutive queries of one head (NW waves x 16 rows)
 //     and walks the causal key range in tiles of 64 keys.  Every K tile (bf16)
 //     and V^T tile (fp16, pre-staged by stage_v) is copied from HBM to LDS once
 //     per workgroup, double-buffered through registers, and read by all waves.
-//   * Each wave computes the transposed score tiles S^T = K Q^T and R^T = K rho^T
-//     with v_mfma_f32_32x32x16_bf16.  One K fragment read from LDS feeds both
-//     MFMAs (the joint QK / RK product).  Q and rho fragments stay in registers.
-//   * In the transposed layout a lane owns one query and 16 keys per 32-key
-//     block, so the online-softmax row reductions are lane-local except for one
-//     exchange with the lane 32 apart.
+//   * Each wave computes the transposed score blocks S^T = K Q^T and R^T = K rho^T
+//     with v_mfma_f32_16x16x32_bf16, 16 keys x 16 queries per block.  One K
+//     fragment read from LDS feeds both MFMAs (the joint QK / RK product).  Q
+//     and rho fragments stay in registers.
+//   * In the transposed layout a lane owns one query and 4 keys per block, so
+//     the online-softmax row reductions are lane-local except for two exchanges
+//     across the four lanes that share a query.
 //   * P = exp2(S*scale*log2e - m) and T = P*R are rounded to fp16 (RNE) and fed,
-//     as B operands, to v_mfma_f32_32x32x16_f16 against the V^T fragment:
+//     as B operands, to v_mfma_f32_16x16x32_f16 against the V^T fragment:
 //     O^T += V^T P^T and A_r^T += V^T T^T, fp32 accumulators in registers.  The
 //     row sums l = sum P and c = sum T are taken from the same rounded values
 //     (v_dot2_f32_f16 against (1,1)), so a single key reproduces v exactly.
-//   * K rows are read into the A operand in a permuted order (bits 2 and 3 of the
-//     row swapped) so that the score accumulators of a lane line up, 8 at a
-//     time, with 8 consecutive keys of the V^T tile: P and T go from the score
-//     MFMA output straight into the value MFMA input without any data movement.
+//   * stage_v stores the keys of every 32-key group of V^T in the order in which
+//     the score accumulators of a lane group come out of two consecutive 16-key
+//     blocks, so P and T go from the score MFMA output straight into the value
+//     MFMA input without any data movement.
+//   * The running max moves lazily: only when some row's tile max exceeds it by
+//     more than kRescaleSlack (log2 units), which makes the rescale of the
+//     accumulators rare after the first tile.
+//   * The register footprint stays within 256 per lane so that two waves share
+//     each SIMD and one wave's MFMAs overlap the other's softmax arithmetic.
 //   * Grid order: the longest (last) query tiles of every head first; heads
 //     cycle fastest so that the 8 XCDs each receive a fixed subset of heads.
 
@@ -34,9 +40,14 @@
 
 namespace plx {
 
-constexpr int PF_BR = 128;      // queries per workgroup
+constexpr int PF_NW = 8;        // waves per workgroup (16 queries each)
+constexpr int PF_BR = 16 * PF_NW;
 constexpr int PF_BC = 64;       // keys per tile
-constexpr int PF_THREADS = 256;
+constexpr int PF_THREADS = 64 * PF_NW;
+// Rescale slack in log2 units: P = 2^(s - m) may grow to 2^kRescaleSlack before
+// the running max m is moved.  Keeps fp16 P <= 16 and T = P*R within fp16 range
+// for |<rho,k>| < 4094.
+constexpr float kRescaleSlack = 4.0f;
 
 template <int D>
 struct PfLayout {
@@ -47,6 +58,14 @@ struct PfLayout {
   static constexpr int STAGE = K_ELEMS + V_ELEMS;   // 2-byte elements per buffer
 };
 
+// Key stored at position p of a 32-key group of a staged V^T tile.  Position
+// 8*g + 4*h + j holds key 16*h + 4*g + j: lane group g of a 16x16 score block
+// owns keys 4g..4g+3 of each block, and two consecutive blocks h = 0, 1 form
+// the 32-key step of the value MFMA.
+__host__ __device__ constexpr int vt_key_of_pos(int p) {
+  return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
+}
+
 template <int D>
 __global__ __launch_bounds__(PF_THREADS, 1)
 void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -54,8 +73,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
                          const float* __restrict__ gate, float* __restrict__ out,
                          int H, int L, int BH, int n_qt, float sl2) {
   using LY = PfLayout<D>;
-  constexpr int KSTEPS = D / 16;                         // MFMA steps over features
-  constexpr int DB = D / 32;                             // 32-feature output blocks
+  constexpr int KSTEPS = D / 32;                         // MFMA steps over features
+  constexpr int FB = D / 16;                             // 16-feature output blocks
   constexpr int KCH = PF_BC * D / 8 / PF_THREADS;        // 16-B K chunks / thread / tile
   constexpr int VCH = D * PF_BC / 8 / PF_THREADS;        // 16-B V^T chunks / thread / tile
   constexpr int KROW_CH = D / 8;                         // 16-B chunks per K row
@@ -65,27 +84,27 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int g = lane >> 5;
+  const int c16 = lane & 15;
+  const int g4 = lane >> 4;
 
   const int qt = n_qt - 1 - (int)(blockIdx.x / (unsigned)BH);
   const int bh = (int)(blockIdx.x % (unsigned)BH);
   const int h = bh % H;
   const int q0 = qt * PF_BR;
-  const int qw0 = q0 + wave * 32;
-  const int qi = qw0 + l32;
+  const int qw0 = q0 + wave * 16;
+  const int qi = qw0 + c16;
   const size_t head = (size_t)bh * L * D;
   const int n_kt_all = (L + PF_BC - 1) / PF_BC;
 
-  // B-operand fragments: query qi, features 16*kk + 8*g .. +7
+  // B-operand fragments: query qi, features 32*kk + 8*g4 .. +7
   bf16x8 qf[KSTEPS], rf[KSTEPS];
   if (qi < L) {
     const bf16x8* qp = reinterpret_cast<const bf16x8*>(q + head + (size_t)qi * D);
     const bf16x8* rp = reinterpret_cast<const bf16x8*>(rho + head + (size_t)qi * D);
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
-      qf[kk] = qp[2 * kk + g];
-      rf[kk] = rp[2 * kk + g];
+      qf[kk] = qp[4 * kk + g4];
+      rf[kk] = rp[4 * kk + g4];
     }
   } else {
 #pragma unroll
@@ -95,17 +114,17 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     }
   }
 
-  f32x16 acc_o[DB], acc_r[DB];
+  f32x4 acc_o[FB], acc_r[FB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    acc_o[db] = f32x16{};
-    acc_r[db] = f32x16{};
+  for (int fb = 0; fb < FB; ++fb) {
+    acc_o[fb] = f32x4{};
+    acc_r[fb] = f32x4{};
   }
   float m_run = kMinit, l_run = 0.f, c_run = 0.f;
 
   const int last_q = min(q0 + PF_BR, L) - 1;
   const int n_kt = last_q / PF_BC + 1;
-  const int wave_last_q = min(qw0 + 31, L - 1);
+  const int wave_last_q = min(qw0 + 15, L - 1);
 
   u32x4 kreg[KCH], vreg[VCH];
   auto load_tile = [&](int kt) {
@@ -140,8 +159,6 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     }
   };
 
-  // A-operand row of this lane inside a 32-key block: bits 2 and 3 swapped
-  const int prow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
   load_tile(0);
@@ -157,72 +174,81 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       const uint16_t* vs = ks + LY::K_ELEMS;
       const bool diag = (k0 + PF_BC - 1 > qw0);
 
-      f32x16 sacc[2], racc[2];
+      // S^T and R^T for four 16-key blocks; lane holds keys 16*kb + 4*g4 + j
+      f32x4 sacc[4], racc[4];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        sacc[b] = f32x16{};
-        racc[b] = f32x16{};
-        const uint16_t* krow = ks + (32 * b + prow) * LY::KS + 8 * g;
+      for (int kb = 0; kb < 4; ++kb) {
+        sacc[kb] = f32x4{};
+        racc[kb] = f32x4{};
+        const uint16_t* krow = ks + (16 * kb + c16) * LY::KS + 8 * g4;
+        bf16x8 a[KSTEPS];
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) a[kk] = *reinterpret_cast<const bf16x8*>(krow + 32 * kk);
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * kk);
-          sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[b], 0, 0, 0);
-          racc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, rf[kk], racc[b], 0, 0, 0);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], qf[kk], sacc[kb], 0, 0, 0);
+          racc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], rf[kk], racc[kb], 0, 0, 0);
         }
       }
 
       // causal mask (diagonal tiles only) and the row maximum
       float mx = kMinit;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
+        for (int j = 0; j < 4; ++j) {
           if (diag) {
-            const int key = k0 + 32 * b + 16 * (e >> 3) + 8 * g + (e & 7);
-            if (key > qi) sacc[b][e] = -INFINITY;
+            const int key = k0 + 16 * kb + 4 * g4 + j;
+            if (key > qi) sacc[kb][j] = -INFINITY;
           }
-          mx = fmaxf(mx, sacc[b][e]);
+          mx = fmaxf(mx, sacc[kb][j]);
         }
       }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * sl2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-      c_run *= alpha;
+      const float m_tile = mx * sl2;
+      if (kt == 0) {
+        m_run = m_tile;                       // accumulators are still zero
+      } else if (__any(m_tile > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, m_tile);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+        c_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        acc_o[db] *= alpha;
-        acc_r[db] *= alpha;
+        for (int fb = 0; fb < FB; ++fb) {
+          acc_o[fb] *= alpha;
+          acc_r[fb] *= alpha;
+        }
       }
+      const float m_use = m_run;
 
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int t = 0; t < 2; ++t) {
+        f16x8 pf, tf;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          f16x8 pf, tf;
+        for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-          for (int e8 = 0; e8 < 8; ++e8) {
-            const int e = 8 * u + e8;
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][e], sl2, -m_new));
-            const float t = p * racc[b][e];
-            pf[e8] = (_Float16)p;
-            tf[e8] = (_Float16)t;
+          for (int j = 0; j < 4; ++j) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[2 * t + hh][j], sl2, -m_use));
+            const float tv = p * racc[2 * t + hh][j];
+            pf[4 * hh + j] = (_Float16)p;
+            tf[4 * hh + j] = (_Float16)tv;
           }
+        }
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const f16x2 pp = {pf[2 * e2], pf[2 * e2 + 1]};
-            const f16x2 tt = {tf[2 * e2], tf[2 * e2 + 1]};
-            l_run = __builtin_amdgcn_fdot2(pp, ones, l_run, false);
-            c_run = __builtin_amdgcn_fdot2(tt, ones, c_run, false);
-          }
-          const uint16_t* vrow = vs + l32 * LY::VS + 16 * (2 * b + u) + 8 * g;
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const f16x2 pp = {pf[2 * e2], pf[2 * e2 + 1]};
+          const f16x2 tt = {tf[2 * e2], tf[2 * e2 + 1]};
+          l_run = __builtin_amdgcn_fdot2(pp, ones, l_run, false);
+          c_run = __builtin_amdgcn_fdot2(tt, ones, c_run, false);
+        }
+        const uint16_t* vrow = vs + c16 * LY::VS + 32 * t + 8 * g4;
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const f16x8 va = *reinterpret_cast<const f16x8*>(vrow + 32 * db * LY::VS);
-            acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf, acc_o[db], 0, 0, 0);
-            acc_r[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, tf, acc_r[db], 0, 0, 0);
-          }
+        for (int fb = 0; fb < FB; ++fb) {
+          const f16x8 va = *reinterpret_cast<const f16x8*>(vrow + 16 * fb * LY::VS);
+          acc_o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pf, acc_o[fb], 0, 0, 0);
+          acc_r[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, tf, acc_r[fb], 0, 0, 0);
         }
       }
     }
@@ -231,31 +257,31 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   }
 
   // epilogue: o = o_sa - g (u - o_sa * rbar), o_sa = O/l, u = A_r/l, rbar = c/l
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float c_tot = c_run + __shfl_xor(c_run, 32);
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  float c_tot = c_run + __shfl_xor(c_run, 16);
+  c_tot += __shfl_xor(c_tot, 32);
   if (qi < L) {
     const float inv = 1.0f / l_tot;
     const float rbar = c_tot * inv;
     const float gh = gate[h];
     float* orow = out + head + (size_t)qi * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int fb = 0; fb < FB; ++fb) {
+      f32x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 o;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float osa = acc_o[db][4 * i + jj] * inv;
-          const float uu = acc_r[db][4 * i + jj] * inv;
-          o[jj] = osa - gh * (uu - osa * rbar);
-        }
-        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * i + 4 * g) = o;
+      for (int j = 0; j < 4; ++j) {
+        const float osa = acc_o[fb][j] * inv;
+        const float uu = acc_r[fb][j] * inv;
+        o[j] = osa - gh * (uu - osa * rbar);
       }
+      *reinterpret_cast<f32x4*>(orow + 16 * fb + 4 * g4) = o;
     }
   }
 }
 
-// V [BH, L, D] bf16 -> V^T tiles [BH][ceil(L/64)][D][64] fp16, zero past L.
+// V [BH, L, D] bf16 -> V^T tiles [BH][ceil(L/64)][D][64] fp16, zero past L, with the
+// keys of each 32-key group in vt_key_of_pos order.
 // One workgroup per (head, 64-key tile): coalesced 16-B loads into LDS, then
 // each thread gathers 8 keys of one feature, converts and stores 16 B.
 template <int D>
@@ -282,7 +308,8 @@ void stage_v_kernel(const __bf16* __restrict__ v, _Float16* __restrict__ vt, int
     f16x8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float x = __uint_as_float((uint32_t)tile[(key0 + e) * PITCH + f] << 16);
+      const int key = vt_key_of_pos(key0 + e);
+      const float x = __uint_as_float((uint32_t)tile[key * PITCH + f] << 16);
       o[e] = (_Float16)x;
     }
     *reinterpret_cast<f16x8*>(dst + (size_t)ch * 8) = o;
