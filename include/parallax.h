@@ -75,7 +75,9 @@ const char* parallax_last_error(void);
  * it on `stream` (stream-ordered allocation).  In PLX_BF16 mode the workspace
  * holds V converted to fp16 in a per-64-key-tile transposed layout (see
  * parallax_prefill_stage_v); the conversion is exact for |v| in
- * [2^-14, 65504] and values must stay below 65504 in magnitude. */
+ * [2^-14, 65504] and values must stay below 65504 in magnitude.  The bf16 path
+ * rounds the softmax numerators P (kept <= 16) and T = P*<rho,k_j> to fp16 for
+ * the value products, so |<rho,k_j>| must stay below 4094. */
 size_t parallax_prefill_workspace_bytes(int B, int H, int L, int d, int dtype);
 
 int parallax_prefill(const void* q, const void* k, const void* v, const void* rho,
@@ -86,7 +88,10 @@ int parallax_prefill(const void* q, const void* k, const void* v, const void* rh
 /* The two stages of a PLX_BF16 prefill, for callers that keep the staged V
  * (for example across several calls over the same keys).
  * stage_v: v [B,H,L,d] bf16 -> vt16, fp16, laid out [B*H][ceil(L/64)][d][64]
- *          (64 consecutive keys of one feature contiguous), keys past L zero.
+ *          (the 64 keys of one tile and one feature contiguous); inside each
+ *          group of 32 keys, position 8a+4b+c (a<4, b<2, c<4) holds key
+ *          16b+4a+c, the order in which the attend kernel's score blocks
+ *          produce them.  Keys past L are zero.
  *          vt16 must hold parallax_prefill_workspace_bytes(B,H,L,d,PLX_BF16).
  * attend : the fused causal forward pass reading V from vt16. */
 int parallax_prefill_stage_v(const void* v, void* vt16, int B, int H, int L, int d,

@@ -40,22 +40,50 @@
 
 namespace plx {
 
-constexpr int PF_NW = 8;        // waves per workgroup (16 queries each)
-constexpr int PF_BR = 16 * PF_NW;
 constexpr int PF_BC = 64;       // keys per tile
-constexpr int PF_THREADS = 64 * PF_NW;
+// waves per workgroup (16 queries each), per head dimension
+#ifndef PLX_PF_NW_D128
+#define PLX_PF_NW_D128 8
+#endif
+#ifndef PLX_PF_NW_D64
+#define PLX_PF_NW_D64 8
+#endif
+// software-pipelined schedule (next tile's scores overlap this tile's softmax)
+#ifndef PLX_PF_PIPE_D128
+#define PLX_PF_PIPE_D128 1
+#endif
+#ifndef PLX_PF_PIPE_D64
+#define PLX_PF_PIPE_D64 0
+#endif
+// minimum waves per SIMD the register allocation must allow, per head dimension
+#ifndef PLX_PF_MINW_D128
+#define PLX_PF_MINW_D128 2
+#endif
+#ifndef PLX_PF_MINW_D64
+#define PLX_PF_MINW_D64 4
+#endif
 // Rescale slack in log2 units: P = 2^(s - m) may grow to 2^kRescaleSlack before
 // the running max m is moved.  Keeps fp16 P <= 16 and T = P*R within fp16 range
 // for |<rho,k>| < 4094.
 constexpr float kRescaleSlack = 4.0f;
 
+// LDS tiles have no padding; 16-byte chunks are XOR-swizzled by row instead,
+// which keeps every fragment read and tile store free of bank conflicts
+// (measured on gfx950: a conflict-free ds_read_b128 occupies the LDS for 4
+// cycles, while a 16-byte row padding still costs 8).
 template <int D>
 struct PfLayout {
-  static constexpr int KS = D + 8;          // LDS row pitch of a K tile (bf16 elements)
-  static constexpr int VS = PF_BC + 8;      // LDS row pitch of a V^T tile (fp16 elements)
-  static constexpr int K_ELEMS = PF_BC * KS;
-  static constexpr int V_ELEMS = D * VS;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;   // 2-byte elements per buffer
+  static constexpr int KCHUNKS = D / 8;        // 16-byte chunks per K row
+  static constexpr int K_ELEMS = PF_BC * D;    // bf16 elements per K tile
+  static constexpr int V_ELEMS = D * PF_BC;    // fp16 elements per V^T tile
+  static constexpr int STAGE = K_ELEMS + V_ELEMS;
+  // element offset of logical 16-byte chunk c of K row r / V^T row r
+  static __device__ __forceinline__ int k_off(int r, int c) {
+    return r * D + ((c ^ (r & (KCHUNKS - 1))) << 3);
+  }
+  static __device__ __forceinline__ int v_off(int r, int c) {
+    return r * PF_BC + ((c ^ (r & 7)) << 3);
+  }
 };
 
 // Key stored at position p of a 32-key group of a staged V^T tile.  Position
@@ -66,18 +94,24 @@ __host__ __device__ constexpr int vt_key_of_pos(int p) {
   return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
 }
 
-template <int D>
-__global__ __launch_bounds__(PF_THREADS, 1)
+// Second launch bound: at least two waves per SIMD, which caps the register
+// budget at 256 per lane and keeps every MFMA operand in VGPRs.
+template <int D, int NW, bool PIPE>
+__global__ __launch_bounds__(64 * NW, (D == 64 ? PLX_PF_MINW_D64 : PLX_PF_MINW_D128))
 void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                          const _Float16* __restrict__ vt, const __bf16* __restrict__ rho,
                          const float* __restrict__ gate, float* __restrict__ out,
                          int H, int L, int BH, int n_qt, float sl2) {
   using LY = PfLayout<D>;
+  constexpr int PF_BR = 16 * NW;                         // queries per workgroup
+  constexpr int PF_THREADS = 64 * NW;
   constexpr int KSTEPS = D / 32;                         // MFMA steps over features
   constexpr int FB = D / 16;                             // 16-feature output blocks
   constexpr int KCH = PF_BC * D / 8 / PF_THREADS;        // 16-B K chunks / thread / tile
   constexpr int VCH = D * PF_BC / 8 / PF_THREADS;        // 16-B V^T chunks / thread / tile
   constexpr int KROW_CH = D / 8;                         // 16-B chunks per K row
+  static_assert(KCH >= 1 && KCH * PF_THREADS * 8 == PF_BC * D, "K tile split");
+  static_assert(VCH >= 1 && VCH * PF_THREADS * 8 == PF_BC * D, "V tile split");
 
   __shared__ __align__(16) uint16_t smem[2 * LY::STAGE];
 
@@ -127,7 +161,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   const int wave_last_q = min(qw0 + 15, L - 1);
 
   u32x4 kreg[KCH], vreg[VCH];
-  auto load_tile = [&](int kt) {
+  auto load_k = [&](int kt) {
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int ch = tid + c * PF_THREADS;
@@ -136,6 +170,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
           ? *reinterpret_cast<const u32x4*>(k + head + (size_t)key * D + (ch % KROW_CH) * 8)
           : u32x4{0u, 0u, 0u, 0u};
     }
+  };
+  auto load_v = [&](int kt) {
     const _Float16* vtile = vt + ((size_t)bh * n_kt_all + kt) * (size_t)(D * PF_BC);
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
@@ -143,73 +179,97 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       vreg[c] = *reinterpret_cast<const u32x4*>(vtile + (size_t)ch * 8);
     }
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = smem + buf * LY::STAGE;
-    uint16_t* vs = ks + LY::K_ELEMS;
+  auto store_k = [&](int buf) {
+    uint16_t* ks = smem + buf * LY::K_ELEMS;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int ch = tid + c * PF_THREADS;
-      *reinterpret_cast<u32x4*>(ks + (ch / KROW_CH) * LY::KS + (ch % KROW_CH) * 8) = kreg[c];
+      *reinterpret_cast<u32x4*>(ks + LY::k_off(ch / KROW_CH, ch % KROW_CH)) = kreg[c];
     }
+  };
+  auto store_v = [&](int buf) {
+    uint16_t* vs = smem + 2 * LY::K_ELEMS + buf * LY::V_ELEMS;
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
       const int ch = tid + c * PF_THREADS;
-      *reinterpret_cast<u32x4*>(vs + (ch / (PF_BC / 8)) * LY::VS + (ch % (PF_BC / 8)) * 8) =
-          vreg[c];
+      *reinterpret_cast<u32x4*>(vs + LY::v_off(ch / (PF_BC / 8), ch % (PF_BC / 8))) = vreg[c];
+    }
+  };
+  // S^T = K Q^T and R^T = K rho^T of one tile; lane holds keys 16*kb + 4*g4 + j
+  auto scores = [&](int buf, f32x4 (&sa)[4], f32x4 (&ra)[4]) {
+    const uint16_t* ks = smem + buf * LY::K_ELEMS;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      bf16x8 a[KSTEPS];
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        a[kk] = *reinterpret_cast<const bf16x8*>(ks + LY::k_off(16 * kb + c16, 4 * kk + g4));
+      sa[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], qf[0], f32x4{}, 0, 0, 0);
+      ra[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], rf[0], f32x4{}, 0, 0, 0);
+#pragma unroll
+      for (int kk = 1; kk < KSTEPS; ++kk) {
+        sa[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], qf[kk], sa[kb], 0, 0, 0);
+        ra[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], rf[kk], ra[kb], 0, 0, 0);
+      }
     }
   };
 
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  // tiles this wave computes: 0 .. n_w-1 (a row always sees key 0 of tile 0)
+  const int n_w = (qw0 < L) ? wave_last_q / PF_BC + 1 : 0;
 
-  load_tile(0);
-  store_tile(0);
+  // K and V tiles are double-buffered.  Pipelined schedule: K runs one tile
+  // ahead of V; in iteration kt the waves read K of tile kt+1 and V of tile kt
+  // while K of tile kt+2 and V of tile kt+1 are written into the buffers read in
+  // iteration kt-1.  Plain schedule: iteration kt reads K and V of tile kt and
+  // writes tile kt+1 into the other buffers.
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  if (PIPE && n_kt > 1) {
+    load_k(1);
+    store_k(1);
+  }
   __syncthreads();
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
-    const int k0 = kt * PF_BC;
-    if (qw0 < L && k0 <= wave_last_q) {
-      const uint16_t* ks = smem + buf * LY::STAGE;
-      const uint16_t* vs = ks + LY::K_ELEMS;
-      const bool diag = (k0 + PF_BC - 1 > qw0);
+  f32x4 sc[4], rc[4];     // scores of the tile being finished
+  if constexpr (PIPE) {
+    if (n_w > 0) scores(0, sc, rc);
+    // iteration 0 overwrites K buffer 0: every wave must be done reading it
+    __syncthreads();
+  }
 
-      // S^T and R^T for four 16-key blocks; lane holds keys 16*kb + 4*g4 + j
-      f32x4 sacc[4], racc[4];
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k_ahead = PIPE ? kt + 2 : kt + 1;
+    if (k_ahead < n_kt) load_k(k_ahead);
+    if (kt + 1 < n_kt) load_v(kt + 1);
+    if (kt < n_w) {
+      const int k0 = kt * PF_BC;
+      const bool diag = (k0 + PF_BC - 1 > qw0);
+      if constexpr (!PIPE) scores(kt & 1, sc, rc);
+      // causal mask (diagonal tiles only) and the row maximum
+      if (__builtin_expect(diag, 0)) {
+        const int lim = qi - k0 - 4 * g4;       // key offset 16*kb + j is kept iff <= lim
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        sacc[kb] = f32x4{};
-        racc[kb] = f32x4{};
-        const uint16_t* krow = ks + (16 * kb + c16) * LY::KS + 8 * g4;
-        bf16x8 a[KSTEPS];
+        for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) a[kk] = *reinterpret_cast<const bf16x8*>(krow + 32 * kk);
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], qf[kk], sacc[kb], 0, 0, 0);
-          racc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], rf[kk], racc[kb], 0, 0, 0);
+          for (int j = 0; j < 4; ++j) {
+            if (16 * kb + j > lim) sc[kb][j] = -INFINITY;
+          }
         }
       }
-
-      // causal mask (diagonal tiles only) and the row maximum
       float mx = kMinit;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (diag) {
-            const int key = k0 + 16 * kb + 4 * g4 + j;
-            if (key > qi) sacc[kb][j] = -INFINITY;
-          }
-          mx = fmaxf(mx, sacc[kb][j]);
-        }
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sc[kb][j]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_tile = mx * sl2;
-      if (kt == 0) {
-        m_run = m_tile;                       // accumulators are still zero
-      } else if (__any(m_tile > m_run + kRescaleSlack)) {
+      if (kt == 0) m_run = m_tile;            // accumulators are still zero
+      if (__any(m_tile > m_run + kRescaleSlack)) {
         const float m_new = fmaxf(m_run, m_tile);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
@@ -223,6 +283,12 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       }
       const float m_use = m_run;
 
+      // scores of the next tile (MFMA) overlap the softmax of this one (VALU);
+      // past the wave's last tile they read a stale buffer and are discarded
+      f32x4 sn[4], rn[4];
+      if constexpr (PIPE) scores((kt + 1) & 1, sn, rn);
+
+      const uint16_t* vs = smem + 2 * LY::K_ELEMS + (kt & 1) * LY::V_ELEMS;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         f16x8 pf, tf;
@@ -230,8 +296,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[2 * t + hh][j], sl2, -m_use));
-            const float tv = p * racc[2 * t + hh][j];
+            const float p = __builtin_amdgcn_exp2f(fmaf(sc[2 * t + hh][j], sl2, -m_use));
+            const float tv = p * rc[2 * t + hh][j];
             pf[4 * hh + j] = (_Float16)p;
             tf[4 * hh + j] = (_Float16)tv;
           }
@@ -243,16 +309,24 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
           l_run = __builtin_amdgcn_fdot2(pp, ones, l_run, false);
           c_run = __builtin_amdgcn_fdot2(tt, ones, c_run, false);
         }
-        const uint16_t* vrow = vs + c16 * LY::VS + 32 * t + 8 * g4;
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb) {
-          const f16x8 va = *reinterpret_cast<const f16x8*>(vrow + 16 * fb * LY::VS);
+          const f16x8 va =
+              *reinterpret_cast<const f16x8*>(vs + LY::v_off(16 * fb + c16, 4 * t + g4));
           acc_o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pf, acc_o[fb], 0, 0, 0);
           acc_r[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, tf, acc_r[fb], 0, 0, 0);
         }
       }
+      if constexpr (PIPE) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          sc[kb] = sn[kb];
+          rc[kb] = rn[kb];
+        }
+      }
     }
-    if (kt + 1 < n_kt) store_tile(buf ^ 1);
+    if (k_ahead < n_kt) store_k(k_ahead & 1);
+    if (kt + 1 < n_kt) store_v((kt + 1) & 1);
     __syncthreads();
   }
 
@@ -328,22 +402,27 @@ hipError_t launch_stage_v(const void* v, void* vt, int BH, int L, int d, hipStre
   return hipGetLastError();
 }
 
+template <int D, int NW, bool PIPE>
+static hipError_t launch_prefill_t(const void* q, const void* k, const void* vt,
+                                   const void* rho, const float* gate, float* out, int B,
+                                   int H, int L, float sl2, hipStream_t s) {
+  const int BH = B * H;
+  const int n_qt = (L + 16 * NW - 1) / (16 * NW);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, PIPE>), dim3((unsigned)(BH * n_qt)), dim3(64 * NW),
+                     0, s, (const __bf16*)q, (const __bf16*)k, (const _Float16*)vt,
+                     (const __bf16*)rho, gate, out, H, L, BH, n_qt, sl2);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* vt, const void* rho,
                                const float* gate, float* out, int B, int H, int L, int d,
                                float scale, hipStream_t s) {
-  const int BH = B * H;
-  const int n_qt = (L + PF_BR - 1) / PF_BR;
-  const dim3 grid((unsigned)(BH * n_qt));
   const float sl2 = scale * kLog2e;
   if (d == 128)
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, dim3(PF_THREADS), 0, s,
-                       (const __bf16*)q, (const __bf16*)k, (const _Float16*)vt,
-                       (const __bf16*)rho, gate, out, H, L, BH, n_qt, sl2);
-  else
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, dim3(PF_THREADS), 0, s,
-                       (const __bf16*)q, (const __bf16*)k, (const _Float16*)vt,
-                       (const __bf16*)rho, gate, out, H, L, BH, n_qt, sl2);
-  return hipGetLastError();
+    return launch_prefill_t<128, PLX_PF_NW_D128, (PLX_PF_PIPE_D128 != 0)>(q, k, vt, rho, gate,
+                                                                          out, B, H, L, sl2, s);
+  return launch_prefill_t<64, PLX_PF_NW_D64, (PLX_PF_PIPE_D64 != 0)>(q, k, vt, rho, gate, out,
+                                                                      B, H, L, sl2, s);
 }
 
 }  // namespace plx
