@@ -14,7 +14,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
 constexpr float kLog2e = 1.4426950408889634f;
+// s_waitcnt immediate for "vmcnt(0)" with expcnt and lgkmcnt left unconstrained
+// (gfx9 encoding: vmcnt[3:0] bits 3:0, expcnt bits 6:4, lgkmcnt bits 11:8,
+// vmcnt[5:4] bits 15:14).
+constexpr int kWaitVmcnt0 = 0x0F70;
 // Running-max sentinel: finite, so that exp2(sentinel - m) is 0 and
 // exp2(sentinel - sentinel) is 1 without NaN from -inf - -inf.
 constexpr float kMinit = -1.0e30f;
@@ -42,6 +49,39 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
   if constexpr (N >= 32) x += __shfl_xor(x, 16);
   return x;
+}
+
+struct Max {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct Sum {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+
+// op(x[lane], x[lane ^ 16]) and op(x[lane], x[lane ^ 32]) for a commutative op.
+// With PLX_PERMLANE_SWAP the exchange uses gfx950's v_permlane{16,32}_swap (a
+// VALU operation: each lane ends up holding both values of its pair across the
+// two results); otherwise a cross-lane shuffle through the LDS crossbar.
+#ifndef PLX_PERMLANE_SWAP
+#define PLX_PERMLANE_SWAP 1
+#endif
+template <class Op>
+__device__ __forceinline__ float lane_xor16(float x, Op op) {
+#if PLX_PERMLANE_SWAP
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+#else
+  return op(x, __shfl_xor(x, 16));
+#endif
+}
+template <class Op>
+__device__ __forceinline__ float lane_xor32(float x, Op op) {
+#if PLX_PERMLANE_SWAP
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+#else
+  return op(x, __shfl_xor(x, 32));
+#endif
 }
 
 }  // namespace plx

@@ -36,6 +36,8 @@
 //   * Grid order: the longest (last) query tiles of every head first; heads
 //     cycle fastest so that the 8 XCDs each receive a fixed subset of heads.
 
+#include <type_traits>
+
 #include "plx_common.h"
 
 namespace plx {
@@ -107,11 +109,6 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   constexpr int PF_THREADS = 64 * NW;
   constexpr int KSTEPS = D / 32;                         // MFMA steps over features
   constexpr int FB = D / 16;                             // 16-feature output blocks
-  constexpr int KCH = PF_BC * D / 8 / PF_THREADS;        // 16-B K chunks / thread / tile
-  constexpr int VCH = D * PF_BC / 8 / PF_THREADS;        // 16-B V^T chunks / thread / tile
-  constexpr int KROW_CH = D / 8;                         // 16-B chunks per K row
-  static_assert(KCH >= 1 && KCH * PF_THREADS * 8 == PF_BC * D, "K tile split");
-  static_assert(VCH >= 1 && VCH * PF_THREADS * 8 == PF_BC * D, "V tile split");
 
   __shared__ __align__(16) uint16_t smem[2 * LY::STAGE];
 
@@ -160,41 +157,44 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   const int n_kt = last_q / PF_BC + 1;
   const int wave_last_q = min(qw0 + 15, L - 1);
 
-  u32x4 kreg[KCH], vreg[VCH];
-  auto load_k = [&](int kt) {
+  // Tiles move HBM -> LDS with global_load_lds_dwordx4: each lane's 16 bytes
+  // land at (wave-uniform base) + 16 * lane, so one wave instruction fills 1 KB
+  // of LDS; the lane's global address picks which logical chunk goes there,
+  // which implements the XOR swizzle without touching registers.
+  constexpr int KBLK = LY::K_ELEMS * 2 / 1024;   // 1-KB blocks per K tile
+  constexpr int VBLK = LY::V_ELEMS * 2 / 1024;   // 1-KB blocks per V^T tile
+  static_assert(KBLK % NW == 0 && VBLK % NW == 0, "tile blocks per wave");
+  auto load_k = [&](int kt, int buf) {
+    // rows past L re-read row L-1: only masked (future) keys meet them
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int ch = tid + c * PF_THREADS;
-      const int key = kt * PF_BC + ch / KROW_CH;
-      kreg[c] = (key < L)
-          ? *reinterpret_cast<const u32x4*>(k + head + (size_t)key * D + (ch % KROW_CH) * 8)
-          : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < KBLK / NW; ++i) {
+      const int blk = i * NW + wave;
+      const int e = blk * 512 + 8 * lane;           // element offset in the tile
+      const int r = e / D, pc = (e % D) / 8;
+      const int c = pc ^ (r & (LY::KCHUNKS - 1));
+      const int key = min(kt * PF_BC + r, L - 1);
+      const __bf16* src = k + head + (size_t)key * D + c * 8;
+      __builtin_amdgcn_global_load_lds((glb_void*)src,
+                                       (lds_void*)(smem + buf * LY::K_ELEMS + blk * 512), 16,
+                                       0, 0);
     }
   };
-  auto load_v = [&](int kt) {
+  auto load_v = [&](int kt, int buf) {
     const _Float16* vtile = vt + ((size_t)bh * n_kt_all + kt) * (size_t)(D * PF_BC);
 #pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int ch = tid + c * PF_THREADS;
-      vreg[c] = *reinterpret_cast<const u32x4*>(vtile + (size_t)ch * 8);
+    for (int i = 0; i < VBLK / NW; ++i) {
+      const int blk = i * NW + wave;
+      const int e = blk * 512 + 8 * lane;
+      const int r = e / PF_BC, pc = (e % PF_BC) / 8;
+      const int c = pc ^ (r & 7);
+      __builtin_amdgcn_global_load_lds((glb_void*)(vtile + r * PF_BC + c * 8),
+                                       (lds_void*)(smem + 2 * LY::K_ELEMS + buf * LY::V_ELEMS +
+                                                   blk * 512),
+                                       16, 0, 0);
     }
   };
-  auto store_k = [&](int buf) {
-    uint16_t* ks = smem + buf * LY::K_ELEMS;
-#pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int ch = tid + c * PF_THREADS;
-      *reinterpret_cast<u32x4*>(ks + LY::k_off(ch / KROW_CH, ch % KROW_CH)) = kreg[c];
-    }
-  };
-  auto store_v = [&](int buf) {
-    uint16_t* vs = smem + 2 * LY::K_ELEMS + buf * LY::V_ELEMS;
-#pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int ch = tid + c * PF_THREADS;
-      *reinterpret_cast<u32x4*>(vs + LY::v_off(ch / (PF_BC / 8), ch % (PF_BC / 8))) = vreg[c];
-    }
-  };
+  // this wave's tile loads have landed in LDS (then a barrier publishes them)
+  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); };
   // S^T = K Q^T and R^T = K rho^T of one tile; lane holds keys 16*kb + 4*g4 + j
   auto scores = [&](int buf, f32x4 (&sa)[4], f32x4 (&ra)[4]) {
     const uint16_t* ks = smem + buf * LY::K_ELEMS;
@@ -223,118 +223,144 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // while K of tile kt+2 and V of tile kt+1 are written into the buffers read in
   // iteration kt-1.  Plain schedule: iteration kt reads K and V of tile kt and
   // writes tile kt+1 into the other buffers.
-  load_k(0);
-  load_v(0);
-  store_k(0);
-  store_v(0);
-  if (PIPE && n_kt > 1) {
-    load_k(1);
-    store_k(1);
-  }
+  load_k(0, 0);
+  load_v(0, 0);
+  if (PIPE && n_kt > 1) load_k(1, 1);
+  wait_loads();
   __syncthreads();
 
   f32x4 sc[4], rc[4];     // scores of the tile being finished
+
+  // Causal mask (the wave's last tile is its only diagonal tile) and the scaled
+  // row max of one tile's scores; the four lanes that share a query combine.
+  auto tile_max = [&](f32x4 (&sa)[4], int kt_, auto diag_c) -> float {
+    if constexpr (decltype(diag_c)::value) {
+      const int lim = qi - kt_ * PF_BC - 4 * g4;   // key offset 16*kb + j is kept iff <= lim
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (16 * kb + j > lim) sa[kb][j] = -INFINITY;
+        }
+      }
+    }
+    float mx = kMinit;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sa[kb][j]);
+    }
+    mx = lane_xor16(mx, Max{});
+    mx = lane_xor32(mx, Max{});
+    return mx * sl2;
+  };
+  // Lazy rescale: the running max only moves when some row's tile max exceeds
+  // it by more than the slack, so P stays below 2^slack.
+  auto rescale_to = [&](float m_tile) {
+    if (__any(m_tile > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      c_run *= alpha;
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        acc_o[fb] *= alpha;
+        acc_r[fb] *= alpha;
+      }
+    }
+  };
+  // P = 2^(S*scale*log2e - m) and T = P*R in fp16, their row sums, and the
+  // value products O^T += V^T P^T, A_r^T += V^T T^T of tile kt_.
+  auto softmax_pv = [&](int kt_) {
+    const float m_use = m_run;
+    const uint16_t* vs = smem + 2 * LY::K_ELEMS + (kt_ & 1) * LY::V_ELEMS;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f16x8 pf, tf;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[2 * t + hh][j], sl2, -m_use));
+          const float tv = p * rc[2 * t + hh][j];
+          pf[4 * hh + j] = (_Float16)p;
+          tf[4 * hh + j] = (_Float16)tv;
+        }
+      }
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const f16x2 pp = {pf[2 * e2], pf[2 * e2 + 1]};
+        const f16x2 tt = {tf[2 * e2], tf[2 * e2 + 1]};
+        l_run = __builtin_amdgcn_fdot2(pp, ones, l_run, false);
+        c_run = __builtin_amdgcn_fdot2(tt, ones, c_run, false);
+      }
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        const f16x8 va =
+            *reinterpret_cast<const f16x8*>(vs + LY::v_off(16 * fb + c16, 4 * t + g4));
+        acc_o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pf, acc_o[fb], 0, 0, 0);
+        acc_r[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, tf, acc_r[fb], 0, 0, 0);
+      }
+    }
+  };
+  // Pipelined step: the score MFMAs of tile kt_+1, the softmax and value MFMAs
+  // of tile kt_, then the mask and max of tile kt_+1 form one basic block, so
+  // the scheduler can overlap MFMA work with the softmax arithmetic and with
+  // the latency of the cross-lane max.  Returns the scaled max of tile kt_+1.
+  auto pipe_step = [&](int kt_, auto diag_next) -> float {
+    f32x4 sn[4], rn[4];
+    scores((kt_ + 1) & 1, sn, rn);
+    softmax_pv(kt_);
+    const float m_next = tile_max(sn, kt_ + 1, diag_next);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      sc[kb] = sn[kb];
+      rc[kb] = rn[kb];
+    }
+    return m_next;
+  };
+
   if constexpr (PIPE) {
-    if (n_w > 0) scores(0, sc, rc);
+    if (n_w > 0) {
+      scores(0, sc, rc);
+      m_run = (n_w == 1) ? tile_max(sc, 0, std::true_type{}) : tile_max(sc, 0, std::false_type{});
+    }
     // iteration 0 overwrites K buffer 0: every wave must be done reading it
     __syncthreads();
   }
 
   for (int kt = 0; kt < n_kt; ++kt) {
+    // Staging is unconditional: past the last tile the loads re-read tile
+    // n_kt-1 into buffers no wave reads again.
     const int k_ahead = PIPE ? kt + 2 : kt + 1;
-    if (k_ahead < n_kt) load_k(k_ahead);
-    if (kt + 1 < n_kt) load_v(kt + 1);
+    load_k(min(k_ahead, n_kt - 1), k_ahead & 1);
+    load_v(min(kt + 1, n_kt - 1), (kt + 1) & 1);
     if (kt < n_w) {
-      const int k0 = kt * PF_BC;
-      const bool diag = (k0 + PF_BC - 1 > qw0);
-      if constexpr (!PIPE) scores(kt & 1, sc, rc);
-      // causal mask (diagonal tiles only) and the row maximum
-      if (__builtin_expect(diag, 0)) {
-        const int lim = qi - k0 - 4 * g4;       // key offset 16*kb + j is kept iff <= lim
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (16 * kb + j > lim) sc[kb][j] = -INFINITY;
-          }
-        }
-      }
-      float mx = kMinit;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sc[kb][j]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_tile = mx * sl2;
-      if (kt == 0) m_run = m_tile;            // accumulators are still zero
-      if (__any(m_tile > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, m_tile);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-        c_run *= alpha;
-#pragma unroll
-        for (int fb = 0; fb < FB; ++fb) {
-          acc_o[fb] *= alpha;
-          acc_r[fb] *= alpha;
-        }
-      }
-      const float m_use = m_run;
-
-      // scores of the next tile (MFMA) overlap the softmax of this one (VALU);
-      // past the wave's last tile they read a stale buffer and are discarded
-      f32x4 sn[4], rn[4];
-      if constexpr (PIPE) scores((kt + 1) & 1, sn, rn);
-
-      const uint16_t* vs = smem + 2 * LY::K_ELEMS + (kt & 1) * LY::V_ELEMS;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        f16x8 pf, tf;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sc[2 * t + hh][j], sl2, -m_use));
-            const float tv = p * rc[2 * t + hh][j];
-            pf[4 * hh + j] = (_Float16)p;
-            tf[4 * hh + j] = (_Float16)tv;
-          }
-        }
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const f16x2 pp = {pf[2 * e2], pf[2 * e2 + 1]};
-          const f16x2 tt = {tf[2 * e2], tf[2 * e2 + 1]};
-          l_run = __builtin_amdgcn_fdot2(pp, ones, l_run, false);
-          c_run = __builtin_amdgcn_fdot2(tt, ones, c_run, false);
-        }
-#pragma unroll
-        for (int fb = 0; fb < FB; ++fb) {
-          const f16x8 va =
-              *reinterpret_cast<const f16x8*>(vs + LY::v_off(16 * fb + c16, 4 * t + g4));
-          acc_o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pf, acc_o[fb], 0, 0, 0);
-          acc_r[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, tf, acc_r[fb], 0, 0, 0);
-        }
-      }
       if constexpr (PIPE) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          sc[kb] = sn[kb];
-          rc[kb] = rn[kb];
+        if (kt + 1 < n_w) {
+          const float m_next = (kt + 2 == n_w) ? pipe_step(kt, std::true_type{})
+                                               : pipe_step(kt, std::false_type{});
+          rescale_to(m_next);
+        } else {
+          softmax_pv(kt);
         }
+      } else {
+        scores(kt & 1, sc, rc);
+        const float m_tile = (kt + 1 == n_w) ? tile_max(sc, kt, std::true_type{})
+                                             : tile_max(sc, kt, std::false_type{});
+        if (kt == 0) m_run = m_tile;            // accumulators are still zero
+        rescale_to(m_tile);
+        softmax_pv(kt);
       }
     }
-    if (k_ahead < n_kt) store_k(k_ahead & 1);
-    if (kt + 1 < n_kt) store_v((kt + 1) & 1);
+    wait_loads();
     __syncthreads();
   }
 
   // epilogue: o = o_sa - g (u - o_sa * rbar), o_sa = O/l, u = A_r/l, rbar = c/l
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  float c_tot = c_run + __shfl_xor(c_run, 16);
-  c_tot += __shfl_xor(c_tot, 32);
+  const float l_tot = lane_xor32(lane_xor16(l_run, Sum{}), Sum{});
+  const float c_tot = lane_xor32(lane_xor16(c_run, Sum{}), Sum{});
   if (qi < L) {
     const float inv = 1.0f / l_tot;
     const float rbar = c_tot * inv;
