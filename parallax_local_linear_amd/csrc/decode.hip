@@ -79,8 +79,9 @@ void decode_split_kernel(const T* __restrict__ q, const T* __restrict__ kc,
     for (int u = 0; u < U; ++u) {
       const int key = c0 + u * KPW + grp;
       if (key < k_end) {
-        kr[u] = *reinterpret_cast<const u32x4*>(kb + (size_t)key * D);
-        vr[u] = *reinterpret_cast<const u32x4*>(vb + (size_t)key * D);
+        // streamed once: non-temporal loads keep the cache stream out of L2
+        kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (size_t)key * D));
+        vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + (size_t)key * D));
       } else {
         kr[u] = u32x4{0u, 0u, 0u, 0u};
         vr[u] = u32x4{0u, 0u, 0u, 0u};
