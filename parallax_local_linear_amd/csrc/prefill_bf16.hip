@@ -45,7 +45,7 @@ namespace plx {
 constexpr int PF_BC = 64;       // keys per tile
 // waves per workgroup (16 queries each), per head dimension
 #ifndef PLX_PF_NW_D128
-#define PLX_PF_NW_D128 8
+#define PLX_PF_NW_D128 4
 #endif
 #ifndef PLX_PF_NW_D64
 #define PLX_PF_NW_D64 8
