@@ -18,6 +18,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Word 3 of a raw (untyped, stride 0) buffer descriptor on gfx9-family parts.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 // s_waitcnt immediate for "vmcnt(0)" with expcnt and lgkmcnt left unconstrained
 // (gfx9 encoding: vmcnt[3:0] bits 3:0, expcnt bits 6:4, lgkmcnt bits 11:8,
 // vmcnt[5:4] bits 15:14).
@@ -49,6 +51,16 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
   if constexpr (N >= 32) x += __shfl_xor(x, 16);
   return x;
+}
+
+// 16 bytes per lane from base + voff into LDS at lds + 16 * lane (lds must be
+// wave-uniform), through a raw buffer descriptor of `bytes` bytes: lanes whose
+// offset is at or past `bytes` write zeros.  (buffer_load_dwordx4 ... lds)
+__device__ __forceinline__ void buffer_load_lds16(const void* base, int bytes, void* lds,
+                                                  uint32_t voff) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferRsrcWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, 0, 0, 0);
 }
 
 struct Max {

@@ -164,34 +164,43 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   constexpr int KBLK = LY::K_ELEMS * 2 / 1024;   // 1-KB blocks per K tile
   constexpr int VBLK = LY::V_ELEMS * 2 / 1024;   // 1-KB blocks per V^T tile
   static_assert(KBLK % NW == 0 && VBLK % NW == 0, "tile blocks per wave");
+  // Tiles move with buffer_load_dwordx4 ... lds.  The per-lane byte offsets of
+  // this wave's 1-KB blocks inside a tile (swizzle included) are the same for
+  // every tile: computed once, one 32-bit register each.  Each load takes a
+  // scalar buffer descriptor based at the tile and sized to the bytes that
+  // exist, so K rows past L come back as zeros from the hardware range check
+  // (they only meet masked, future keys).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t koff[KBLK / NW], voff[VBLK / NW];
+#pragma unroll
+  for (int i = 0; i < KBLK / NW; ++i) {
+    const int e = (i * NW + wave) * 512 + 8 * lane;   // element offset in the tile
+    const int r = e / D, pc = (e % D) / 8;
+    koff[i] = (uint32_t)((r * D + ((pc ^ (r & (LY::KCHUNKS - 1))) << 3)) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < VBLK / NW; ++i) {
+    const int e = (i * NW + wave) * 512 + 8 * lane;
+    const int r = e / PF_BC, pc = (e % PF_BC) / 8;
+    voff[i] = (uint32_t)((r * PF_BC + ((pc ^ (r & 7)) << 3)) * 2);
+  }
+  const char* kbase = reinterpret_cast<const char*>(k + head);
   auto load_k = [&](int kt, int buf) {
-    // rows past L re-read row L-1: only masked (future) keys meet them
+    const int rows = min(PF_BC, L - kt * PF_BC);
+    const char* tile = kbase + (size_t)kt * PF_BC * D * 2;
 #pragma unroll
-    for (int i = 0; i < KBLK / NW; ++i) {
-      const int blk = i * NW + wave;
-      const int e = blk * 512 + 8 * lane;           // element offset in the tile
-      const int r = e / D, pc = (e % D) / 8;
-      const int c = pc ^ (r & (LY::KCHUNKS - 1));
-      const int key = min(kt * PF_BC + r, L - 1);
-      const __bf16* src = k + head + (size_t)key * D + c * 8;
-      __builtin_amdgcn_global_load_lds((glb_void*)src,
-                                       (lds_void*)(smem + buf * LY::K_ELEMS + blk * 512), 16,
-                                       0, 0);
-    }
+    for (int i = 0; i < KBLK / NW; ++i)
+      buffer_load_lds16(tile, rows * D * 2, smem + buf * LY::K_ELEMS + (i * NW + wave_u) * 512,
+                        koff[i]);
   };
+  const char* vbase = reinterpret_cast<const char*>(vt + (size_t)bh * n_kt_all * (D * PF_BC));
   auto load_v = [&](int kt, int buf) {
-    const _Float16* vtile = vt + ((size_t)bh * n_kt_all + kt) * (size_t)(D * PF_BC);
+    const char* tile = vbase + (size_t)kt * (D * PF_BC) * 2;
 #pragma unroll
-    for (int i = 0; i < VBLK / NW; ++i) {
-      const int blk = i * NW + wave;
-      const int e = blk * 512 + 8 * lane;
-      const int r = e / PF_BC, pc = (e % PF_BC) / 8;
-      const int c = pc ^ (r & 7);
-      __builtin_amdgcn_global_load_lds((glb_void*)(vtile + r * PF_BC + c * 8),
-                                       (lds_void*)(smem + 2 * LY::K_ELEMS + buf * LY::V_ELEMS +
-                                                   blk * 512),
-                                       16, 0, 0);
-    }
+    for (int i = 0; i < VBLK / NW; ++i)
+      buffer_load_lds16(tile, D * PF_BC * 2,
+                        smem + 2 * LY::K_ELEMS + buf * LY::V_ELEMS + (i * NW + wave_u) * 512,
+                        voff[i]);
   };
   // this wave's tile loads have landed in LDS (then a barrier publishes them)
   auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); };
