@@ -11,7 +11,8 @@
 //   * A workgroup owns 16*NW consecutive queries of one head (NW waves x 16 rows)
 //     and walks the causal key range in tiles of 64 keys.  Every K tile (bf16)
 //     and V^T tile (fp16, pre-staged by stage_v) is copied from HBM to LDS once
-//     per workgroup, double-buffered through registers, and read by all waves.
+//     per workgroup by buffer loads that write LDS directly, double-buffered,
+//     and read by all waves.
 //   * Each wave computes the transposed score blocks S^T = K Q^T and R^T = K rho^T
 //     with v_mfma_f32_16x16x32_bf16, 16 keys x 16 queries per block.  One K
 //     fragment read from LDS feeds both MFMAs (the joint QK / RK product).  Q
@@ -320,6 +321,10 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   auto pipe_step = [&](int kt_, auto diag_next) -> float {
     f32x4 sn[4], rn[4];
     scores((kt_ + 1) & 1, sn, rn);
+    // The V tile of the next step is staged here rather than at the top of the
+    // iteration: the wave's vector-memory issue then overlaps its score MFMAs
+    // instead of delaying them.
+    load_v(min(kt_ + 1, n_kt - 1), (kt_ + 1) & 1);
     softmax_pv(kt_);
     const float m_next = tile_max(sn, kt_ + 1, diag_next);
 #pragma unroll
@@ -344,7 +349,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     // n_kt-1 into buffers no wave reads again.
     const int k_ahead = PIPE ? kt + 2 : kt + 1;
     load_k(min(k_ahead, n_kt - 1), k_ahead & 1);
-    load_v(min(kt + 1, n_kt - 1), (kt + 1) & 1);
+    const bool v_in_step = PIPE && kt + 1 < n_w;     // pipe_step stages V itself
+    if (!v_in_step) load_v(min(kt + 1, n_kt - 1), (kt + 1) & 1);
     if (kt < n_w) {
       if constexpr (PIPE) {
         if (kt + 1 < n_w) {
