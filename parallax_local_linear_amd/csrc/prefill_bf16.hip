@@ -206,8 +206,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // this wave's tile loads have landed in LDS (then a barrier publishes them)
   auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); };
   // S^T = K Q^T and R^T = K rho^T of one tile; lane holds keys 16*kb + 4*g4 + j
-  auto scores = [&](int buf, f32x4 (&sa)[4], f32x4 (&ra)[4]) {
-    const uint16_t* ks = smem + buf * LY::K_ELEMS;
+  auto scores = [&](auto buf, f32x4 (&sa)[4], f32x4 (&ra)[4]) {
+    const uint16_t* ks = smem + (int)buf * LY::K_ELEMS;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       bf16x8 a[KSTEPS];
@@ -282,9 +282,9 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   };
   // P = 2^(S*scale*log2e - m) and T = P*R in fp16, their row sums, and the
   // value products O^T += V^T P^T, A_r^T += V^T T^T of tile kt_.
-  auto softmax_pv = [&](int kt_) {
+  auto softmax_pv = [&](auto vbuf, f32x4 (&sa)[4], f32x4 (&ra)[4]) {
     const float m_use = m_run;
-    const uint16_t* vs = smem + 2 * LY::K_ELEMS + (kt_ & 1) * LY::V_ELEMS;
+    const uint16_t* vs = smem + 2 * LY::K_ELEMS + (int)vbuf * LY::V_ELEMS;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f16x8 pf, tf;
@@ -292,8 +292,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc[2 * t + hh][j], sl2, -m_use));
-          const float tv = p * rc[2 * t + hh][j];
+          const float p = __builtin_amdgcn_exp2f(fmaf(sa[2 * t + hh][j], sl2, -m_use));
+          const float tv = p * ra[2 * t + hh][j];
           pf[4 * hh + j] = (_Float16)p;
           tf[4 * hh + j] = (_Float16)tv;
         }
@@ -318,59 +318,65 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // of tile kt_, then the mask and max of tile kt_+1 form one basic block, so
   // the scheduler can overlap MFMA work with the softmax arithmetic and with
   // the latency of the cross-lane max.  Returns the scaled max of tile kt_+1.
-  auto pipe_step = [&](int kt_, auto diag_next) -> float {
-    f32x4 sn[4], rn[4];
-    scores((kt_ + 1) & 1, sn, rn);
+  // `par` is the parity of kt_: it names the buffers at compile time, and the
+  // loop below alternates the two score register sets instead of copying.
+  auto pipe_step = [&](int kt_, auto par, auto diag_next, f32x4 (&cs)[4], f32x4 (&cr)[4],
+                       f32x4 (&ns)[4], f32x4 (&nr)[4]) -> float {
+    constexpr int P = decltype(par)::value;
+    scores(std::integral_constant<int, 1 - P>{}, ns, nr);
     // The V tile of the next step is staged here rather than at the top of the
     // iteration: the wave's vector-memory issue then overlaps its score MFMAs
     // instead of delaying them.
-    load_v(min(kt_ + 1, n_kt - 1), (kt_ + 1) & 1);
-    softmax_pv(kt_);
-    const float m_next = tile_max(sn, kt_ + 1, diag_next);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      sc[kb] = sn[kb];
-      rc[kb] = rn[kb];
-    }
-    return m_next;
+    load_v(min(kt_ + 1, n_kt - 1), 1 - P);
+    softmax_pv(par, cs, cr);
+    return tile_max(ns, kt_ + 1, diag_next);
   };
 
+  f32x4 sn[4], rn[4];     // the other score register set of the pipelined loop
   if constexpr (PIPE) {
     if (n_w > 0) {
-      scores(0, sc, rc);
+      scores(std::integral_constant<int, 0>{}, sc, rc);
       m_run = (n_w == 1) ? tile_max(sc, 0, std::true_type{}) : tile_max(sc, 0, std::false_type{});
     }
     // iteration 0 overwrites K buffer 0: every wave must be done reading it
     __syncthreads();
   }
 
-  for (int kt = 0; kt < n_kt; ++kt) {
+  // One iteration of the tile loop; kt has parity P.
+  auto iteration = [&](int kt, auto par, f32x4 (&cs)[4], f32x4 (&cr)[4], f32x4 (&ns)[4],
+                       f32x4 (&nr)[4]) {
+    constexpr int P = decltype(par)::value;
     // Staging is unconditional: past the last tile the loads re-read tile
     // n_kt-1 into buffers no wave reads again.
     const int k_ahead = PIPE ? kt + 2 : kt + 1;
-    load_k(min(k_ahead, n_kt - 1), k_ahead & 1);
+    load_k(min(k_ahead, n_kt - 1), PIPE ? P : 1 - P);
     const bool v_in_step = PIPE && kt + 1 < n_w;     // pipe_step stages V itself
-    if (!v_in_step) load_v(min(kt + 1, n_kt - 1), (kt + 1) & 1);
+    if (!v_in_step) load_v(min(kt + 1, n_kt - 1), 1 - P);
     if (kt < n_w) {
       if constexpr (PIPE) {
         if (kt + 1 < n_w) {
-          const float m_next = (kt + 2 == n_w) ? pipe_step(kt, std::true_type{})
-                                               : pipe_step(kt, std::false_type{});
+          const float m_next =
+              (kt + 2 == n_w) ? pipe_step(kt, par, std::true_type{}, cs, cr, ns, nr)
+                              : pipe_step(kt, par, std::false_type{}, cs, cr, ns, nr);
           rescale_to(m_next);
         } else {
-          softmax_pv(kt);
+          softmax_pv(par, cs, cr);
         }
       } else {
-        scores(kt & 1, sc, rc);
-        const float m_tile = (kt + 1 == n_w) ? tile_max(sc, kt, std::true_type{})
-                                             : tile_max(sc, kt, std::false_type{});
+        scores(par, cs, cr);
+        const float m_tile = (kt + 1 == n_w) ? tile_max(cs, kt, std::true_type{})
+                                             : tile_max(cs, kt, std::false_type{});
         if (kt == 0) m_run = m_tile;            // accumulators are still zero
         rescale_to(m_tile);
-        softmax_pv(kt);
+        softmax_pv(par, cs, cr);
       }
     }
     wait_loads();
     __syncthreads();
+  };
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    iteration(kt, std::integral_constant<int, 0>{}, sc, rc, sn, rn);
+    if (kt + 1 < n_kt) iteration(kt + 1, std::integral_constant<int, 1>{}, sn, rn, sc, rc);
   }
 
   // epilogue: o = o_sa - g (u - o_sa * rbar), o_sa = O/l, u = A_r/l, rbar = c/l
