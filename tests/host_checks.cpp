@@ -1,0 +1,183 @@
+// Host-side checks of the C ABI, built with AddressSanitizer and
+// UndefinedBehaviorSanitizer around the library's host code (tests/test_host_sanitized.py).
+//
+// Every call here is rejected by argument validation before anything touches a
+// device pointer, except the "no device" block, which only runs when the HIP
+// runtime reports no device: there the launch and allocation failures must come
+// back as PLX_EHIP / PLX_ENOMEM with an error text.  Exit status = number of
+// failed checks.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+
+#include "parallax.h"
+
+namespace {
+
+int g_failed = 0;
+
+void check(bool cond, const char* what) {
+  if (!cond) {
+    std::printf("FAIL: %s (last error: \"%s\")\n", what, parallax_last_error());
+    ++g_failed;
+  }
+}
+
+// status matches and the error text names the entry point
+void expect(int st, int want, const char* fn, const char* what) {
+  const std::string msg = parallax_last_error();
+  if (st != want || msg.find(fn) == std::string::npos) {
+    std::printf("FAIL: %s: status %d (want %d), error \"%s\"\n", what, st, want, msg.c_str());
+    ++g_failed;
+  }
+}
+
+// Distinct non-null addresses that are never dereferenced by the rejected calls.
+char g_dummy[64];
+void* P(int i) { return g_dummy + i; }
+float* F(int i) { return reinterpret_cast<float*>(g_dummy + 4 * i); }
+const int32_t* I(int i) { return reinterpret_cast<const int32_t*>(g_dummy + 4 * i); }
+
+size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
+
+void workspace_sizes() {
+  for (int d : {64, 128})
+    for (int L : {1, 63, 64, 65, 4096}) {
+      const size_t want = (size_t)3 * 5 * ceil_div(L, 64) * 64 * d * 2;
+      check(parallax_prefill_workspace_bytes(3, 5, L, d, PLX_BF16) == want,
+            "prefill workspace = B*H*ceil(L/64)*64*d*2 bytes");
+      check(parallax_prefill_workspace_bytes(3, 5, L, d, PLX_F32) == 0,
+            "fp32 prefill needs no workspace");
+    }
+  check(parallax_prefill_workspace_bytes(0, 1, 64, 64, PLX_BF16) == 0, "B=0 workspace is 0");
+  check(parallax_prefill_workspace_bytes(1, 1, 64, 96, PLX_BF16) == 0, "d=96 workspace is 0");
+  for (int d : {64, 128})
+    for (int Lmax : {1, 1000, 8192, 131072}) {
+      const size_t want = (size_t)2 * 3 * ceil_div(Lmax, 1024) * (2 * d + 4) * 4;
+      check(parallax_decode_workspace_bytes(2, 3, Lmax, d, 1024) == want,
+            "decode workspace = B*H*ceil(Lmax/C)*(2d+4)*4 bytes");
+      const int C = parallax_decode_default_split(2, 3, Lmax, d);
+      check(C >= 256 && C % 64 == 0, "default split is a multiple of 64, at least 256");
+      check(parallax_decode_workspace_bytes(2, 3, Lmax, d, 0) ==
+                parallax_decode_workspace_bytes(2, 3, Lmax, d, C),
+            "split 0 sizes the workspace for the default split");
+    }
+  check(parallax_decode_workspace_bytes(1, 1, 1024, 128, 100) == 0,
+        "split not a multiple of 64 gives 0");
+}
+
+void prefill_rejections() {
+  const char* fn = "parallax_prefill";
+  expect(parallax_prefill(P(0), P(1), P(2), P(3), F(4), F(5), 0, 1, 64, 64, 0.f, PLX_BF16,
+                          nullptr, 0, nullptr), PLX_EINVAL, fn, "prefill B=0");
+  expect(parallax_prefill(P(0), P(1), P(2), P(3), F(4), F(5), 1, 1, 0, 64, 0.f, PLX_BF16,
+                          nullptr, 0, nullptr), PLX_EINVAL, fn, "prefill L=0");
+  expect(parallax_prefill(P(0), P(1), P(2), P(3), F(4), F(5), 1, 1, 64, 96, 0.f, PLX_BF16,
+                          nullptr, 0, nullptr), PLX_EUNSUPPORTED, fn, "prefill d=96");
+  expect(parallax_prefill(P(0), P(1), P(2), P(3), F(4), F(5), 1, 1, 64, 64, 0.f, 7, nullptr, 0,
+                          nullptr), PLX_EUNSUPPORTED, fn, "prefill dtype 7");
+  expect(parallax_prefill(nullptr, P(1), P(2), P(3), F(4), F(5), 1, 1, 64, 64, 0.f, PLX_BF16,
+                          nullptr, 0, nullptr), PLX_EINVAL, fn, "prefill null q");
+  expect(parallax_prefill(P(0), P(1), P(2), P(3), nullptr, F(5), 1, 1, 64, 64, 0.f, PLX_F32,
+                          nullptr, 0, nullptr), PLX_EINVAL, fn, "prefill null gate");
+  const size_t need = parallax_prefill_workspace_bytes(2, 2, 100, 128, PLX_BF16);
+  expect(parallax_prefill(P(0), P(1), P(2), P(3), F(4), F(5), 2, 2, 100, 128, 0.f, PLX_BF16,
+                          P(6), need - 1, nullptr), PLX_EINVAL, fn, "prefill workspace too small");
+  expect(parallax_prefill(P(0), P(1), P(2), P(3), F(4), F(5), 65535, 65535, 1 << 20, 128, 0.f,
+                          PLX_BF16, nullptr, 0, nullptr), PLX_EINVAL, fn, "prefill too large");
+  expect(parallax_prefill_stage_v(nullptr, P(1), 1, 1, 64, 64, nullptr), PLX_EINVAL,
+         "parallax_prefill_stage_v", "stage_v null v");
+  expect(parallax_prefill_stage_v(P(0), P(1), 1, -2, 64, 64, nullptr), PLX_EINVAL,
+         "parallax_prefill_stage_v", "stage_v H<0");
+  expect(parallax_prefill_attend(P(0), P(1), P(2), P(3), F(4), nullptr, 1, 1, 64, 128, 0.f,
+                                 nullptr), PLX_EINVAL, "parallax_prefill_attend",
+         "attend null out");
+  expect(parallax_prefill_attend(P(0), P(1), P(2), P(3), F(4), F(5), 1, 1, 64, 32, 0.f, nullptr),
+         PLX_EUNSUPPORTED, "parallax_prefill_attend", "attend d=32");
+}
+
+void decode_rejections() {
+  const char* fn = "parallax_decode";
+  expect(parallax_decode(P(0), P(1), P(2), P(3), F(4), F(5), I(6), 1, 1, 0, 128, 0.f, PLX_BF16,
+                         0, nullptr, 0, nullptr), PLX_EINVAL, fn, "decode Lmax=0");
+  expect(parallax_decode(P(0), P(1), P(2), P(3), F(4), F(5), I(6), 300, 300, 64, 128, 0.f,
+                         PLX_BF16, 0, nullptr, 0, nullptr), PLX_EINVAL, fn, "decode B*H > 65535");
+  expect(parallax_decode(P(0), P(1), P(2), P(3), F(4), F(5), I(6), 1, 1, 64, 128, 0.f, PLX_BF16,
+                         100, nullptr, 0, nullptr), PLX_EINVAL, fn, "decode split 100");
+  expect(parallax_decode(P(0), P(1), P(2), P(3), F(4), F(5), I(6), 1, 1, 64, 128, 0.f, PLX_BF16,
+                         -64, nullptr, 0, nullptr), PLX_EINVAL, fn, "decode split -64");
+  expect(parallax_decode(P(0), P(1), P(2), P(3), F(4), F(5), nullptr, 1, 1, 64, 128, 0.f,
+                         PLX_BF16, 0, nullptr, 0, nullptr), PLX_EINVAL, fn, "decode null seqlens");
+  expect(parallax_decode(P(0), P(1), P(2), P(3), F(4), F(5), I(6), 1, 1, 64, 128, 0.f, 3, 0,
+                         nullptr, 0, nullptr), PLX_EUNSUPPORTED, fn, "decode dtype 3");
+  const size_t need = parallax_decode_workspace_bytes(4, 2, 5000, 64, 512);
+  expect(parallax_decode(P(0), P(1), P(2), P(3), F(4), F(5), I(6), 4, 2, 5000, 64, 0.f, PLX_BF16,
+                         512, P(7), need - 4, nullptr), PLX_EINVAL, fn,
+         "decode workspace too small");
+  expect(parallax_decode_partials(P(0), P(1), P(2), P(3), I(4), F(5), 1, 1, 64, 64, 0.f,
+                                  PLX_BF16, 0, nullptr), PLX_EINVAL, "parallax_decode_partials",
+         "partials need an explicit split");
+  expect(parallax_decode_combine(nullptr, F(1), I(2), F(3), 1, 1, 64, 64, 64, nullptr),
+         PLX_EINVAL, "parallax_decode_combine", "combine null partials");
+  expect(parallax_decode_combine(F(0), F(1), I(2), F(3), 1, 1, 64, 64, 96, nullptr), PLX_EINVAL,
+         "parallax_decode_combine", "combine split 96");
+}
+
+// Without a device, valid arguments reach the HIP runtime: the launch and
+// allocation failures must be reported, not crash.
+void no_device_failures() {
+  const size_t ws = parallax_prefill_workspace_bytes(1, 1, 64, 64, PLX_BF16);
+  expect(parallax_prefill(P(0), P(1), P(2), P(3), F(4), F(5), 1, 1, 64, 64, 0.f, PLX_BF16, P(6),
+                          ws, nullptr), PLX_EHIP, "parallax_prefill", "prefill launch failure");
+  expect(parallax_prefill(P(0), P(1), P(2), P(3), F(4), F(5), 1, 1, 64, 64, 0.f, PLX_BF16,
+                          nullptr, 0, nullptr), PLX_ENOMEM, "parallax_prefill",
+         "prefill allocation failure");
+  expect(parallax_prefill(P(0), P(1), P(2), P(3), F(4), F(5), 1, 1, 64, 64, 0.f, PLX_F32,
+                          nullptr, 0, nullptr), PLX_EHIP, "parallax_prefill",
+         "fp32 prefill launch failure");
+  expect(parallax_prefill_stage_v(P(0), P(1), 1, 1, 64, 64, nullptr), PLX_EHIP,
+         "parallax_prefill_stage_v", "stage_v launch failure");
+  expect(parallax_prefill_attend(P(0), P(1), P(2), P(3), F(4), F(5), 1, 1, 64, 64, 0.f, nullptr),
+         PLX_EHIP, "parallax_prefill_attend", "attend launch failure");
+  expect(parallax_decode(P(0), P(1), P(2), P(3), F(4), F(5), I(6), 1, 1, 64, 128, 0.f, PLX_BF16,
+                         0, nullptr, 0, nullptr), PLX_ENOMEM, "parallax_decode",
+         "decode allocation failure");
+  const size_t dws = parallax_decode_workspace_bytes(1, 1, 64, 128, 64);
+  expect(parallax_decode(P(0), P(1), P(2), P(3), F(4), F(5), I(6), 1, 1, 64, 128, 0.f, PLX_BF16,
+                         64, P(7), dws, nullptr), PLX_EHIP, "parallax_decode",
+         "decode launch failure");
+  expect(parallax_decode_partials(P(0), P(1), P(2), P(3), I(4), F(5), 1, 1, 64, 64, 0.f,
+                                  PLX_F32, 64, nullptr), PLX_EHIP, "parallax_decode_partials",
+         "partials launch failure");
+  expect(parallax_decode_combine(F(0), F(1), I(2), F(3), 1, 1, 64, 64, 64, nullptr), PLX_EHIP,
+         "parallax_decode_combine", "combine launch failure");
+}
+
+void error_text_is_per_thread() {
+  expect(parallax_prefill_stage_v(nullptr, P(1), 1, 1, 64, 64, nullptr), PLX_EINVAL,
+         "parallax_prefill_stage_v", "error on the main thread");
+  std::string other = "unset";
+  std::thread t([&] { other = parallax_last_error(); });
+  t.join();
+  check(other.empty(), "another thread does not see this thread's error text");
+  check(std::strlen(parallax_last_error()) > 0, "this thread keeps its error text");
+}
+
+}  // namespace
+
+int main() {
+  check(parallax_abi_version() == PARALLAX_ABI_VERSION, "ABI version");
+  workspace_sizes();
+  prefill_rejections();
+  decode_rejections();
+  error_text_is_per_thread();
+  int n_dev = 0;
+  if (hipGetDeviceCount(&n_dev) != hipSuccess) n_dev = 0;
+  if (n_dev == 0) no_device_failures();
+  else std::printf("a device is present: the no-device failure checks are skipped\n");
+  std::printf("%d failed\n", g_failed);
+  return g_failed;
+}
