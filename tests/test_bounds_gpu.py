@@ -1,0 +1,152 @@
+"""No kernel writes outside its outputs, and no kernel writes its inputs.
+
+Every output and workspace is placed inside a larger buffer whose guard bands
+(4 KiB on each side) hold a sentinel pattern; after the call the guard bands
+must be unchanged, every element of an output must have been written, and the
+inputs must be bit-identical to their copies taken before the call.  Calls go
+through the raw C ABI with pointers into the guarded buffers.
+"""
+import pytest
+import torch
+
+import workloads as wl
+from parallax_local_linear_amd import _native
+
+pytestmark = pytest.mark.gpu
+
+PAD = 4096                      # guard band, bytes (keeps 16-byte alignment)
+SENT = 0xA5                     # sentinel byte; as fp32 it reads -2.9e-16, never an output
+
+
+def _guarded(nbytes):
+    buf = torch.full((PAD + nbytes + PAD,), SENT, dtype=torch.uint8, device="cuda")
+    return buf, buf.data_ptr() + PAD
+
+
+def _check_guards(buf, nbytes, what, fully_written=True):
+    head, body, tail = buf[:PAD], buf[PAD:PAD + nbytes], buf[PAD + nbytes:]
+    assert bool((head == SENT).all()), f"{what}: write before the buffer"
+    assert bool((tail == SENT).all()), f"{what}: write past the end of the buffer"
+    if fully_written:
+        words = body.view(torch.int32)
+        assert not bool((words == int.from_bytes(bytes([SENT]) * 4, "little", signed=True)).any()), \
+            f"{what}: some elements were never written"
+
+
+def _snapshot(inp):
+    return {k: v.clone() for k, v in inp.items() if torch.is_tensor(v)}
+
+
+def _unchanged(inp, snap):
+    for k, v in snap.items():
+        assert torch.equal(inp[k].view(torch.uint8), v.view(torch.uint8)), f"input {k} was modified"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("L", [1, 65, 200])
+def test_prefill_writes_stay_in_bounds(dtype, d, L):
+    lib = _native.lib()
+    B, H = 2, 3
+    inp = wl.prefill_inputs(B, H, L, d, dtype, seed=600 + L + d, device="cuda", rho_std=0.5,
+                            gate=("uniform", 0.2, 1.0))
+    snap = _snapshot(inp)
+    out_bytes = B * H * L * d * 4
+    out_buf, out_ptr = _guarded(out_bytes)
+    code = _native.PLX_BF16 if dtype == "bf16" else _native.PLX_F32
+    ws_bytes = lib.parallax_prefill_workspace_bytes(B, H, L, d, code)
+    ws_buf, ws_ptr = _guarded(ws_bytes) if ws_bytes else (None, None)
+    st = lib.parallax_prefill(inp["q"].data_ptr(), inp["k"].data_ptr(), inp["v"].data_ptr(),
+                              inp["rho"].data_ptr(), inp["gate"].data_ptr(), out_ptr,
+                              B, H, L, d, 0.0, code, ws_ptr, ws_bytes,
+                              torch.cuda.current_stream().cuda_stream)
+    assert st == 0, lib.parallax_last_error()
+    torch.cuda.synchronize()
+    _check_guards(out_buf, out_bytes, "prefill out")
+    if ws_buf is not None:
+        # the staged V^T covers whole 64-key tiles, zero past L: every byte written
+        _check_guards(ws_buf, ws_bytes, "prefill workspace")
+    _unchanged(inp, snap)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_writes_stay_in_bounds(dtype, d):
+    lib = _native.lib()
+    B, H, Lmax, split = 3, 2, 700, 128
+    inp = wl.decode_inputs(B, H, Lmax, d, dtype, seed=610 + d, device="cuda",
+                           seqlens=[700, 129, 0])
+    snap = _snapshot(inp)
+    code = _native.PLX_BF16 if dtype == "bf16" else _native.PLX_F32
+    out_bytes = B * H * d * 4
+    stream = torch.cuda.current_stream().cuda_stream
+    # one call with a library-sized workspace
+    out_buf, out_ptr = _guarded(out_bytes)
+    ws_bytes = lib.parallax_decode_workspace_bytes(B, H, Lmax, d, split)
+    ws_buf, ws_ptr = _guarded(ws_bytes)
+    st = lib.parallax_decode(inp["q"].data_ptr(), inp["kcache"].data_ptr(),
+                             inp["vcache"].data_ptr(), inp["rho"].data_ptr(),
+                             inp["gate"].data_ptr(), out_ptr, inp["seqlens"].data_ptr(),
+                             B, H, Lmax, d, 0.0, code, split, ws_ptr, ws_bytes, stream)
+    assert st == 0, lib.parallax_last_error()
+    torch.cuda.synchronize()
+    _check_guards(out_buf, out_bytes, "decode out")
+    # split records exist only for splits that hold keys: the rest may stay unwritten
+    _check_guards(ws_buf, ws_bytes, "decode workspace", fully_written=False)
+    _unchanged(inp, snap)
+    # the two stages separately, into guarded partials
+    part_buf, part_ptr = _guarded(ws_bytes)
+    out2_buf, out2_ptr = _guarded(out_bytes)
+    st = lib.parallax_decode_partials(inp["q"].data_ptr(), inp["kcache"].data_ptr(),
+                                      inp["vcache"].data_ptr(), inp["rho"].data_ptr(),
+                                      inp["seqlens"].data_ptr(), part_ptr, B, H, Lmax, d, 0.0,
+                                      code, split, stream)
+    assert st == 0, lib.parallax_last_error()
+    st = lib.parallax_decode_combine(part_ptr, inp["gate"].data_ptr(), inp["seqlens"].data_ptr(),
+                                     out2_ptr, B, H, Lmax, d, split, stream)
+    assert st == 0, lib.parallax_last_error()
+    torch.cuda.synchronize()
+    _check_guards(part_buf, ws_bytes, "decode partials", fully_written=False)
+    _check_guards(out2_buf, out_bytes, "decode combine out")
+    assert torch.equal(out_buf[PAD:PAD + out_bytes], out2_buf[PAD:PAD + out_bytes])
+    _unchanged(inp, snap)
+
+
+def test_nan_in_a_query_row_stays_in_that_row():
+    """A NaN in one query row turns that output row into NaN.  Rows outside its
+    16-row block (one wave) are bit-identical to a clean run; rows inside it
+    agree within the parity tolerance (the wave's shared rescale schedule may
+    differ, which moves the fp16 rounding of P)."""
+    import parallax_local_linear_amd as plx
+    inp = wl.prefill_inputs(1, 2, 130, 128, "bf16", seed=620, device="cuda", rho_std=0.5)
+    clean = plx.prefill(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"])
+    q = inp["q"].clone()
+    q[0, 1, 70, 5] = float("nan")
+    out = plx.prefill(q, inp["k"], inp["v"], inp["rho"], inp["gate"])
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(out[0, 1, 70]).all())
+    block = torch.zeros(out.shape[:3], dtype=torch.bool, device="cuda")
+    block[0, 1, 64:80] = True
+    block[0, 1, 70] = False
+    other = torch.ones_like(block)
+    other[0, 1, 64:80] = False
+    assert torch.equal(out[other], clean[other])
+    assert bool(torch.isfinite(out[block]).all())
+    assert float((out[block] - clean[block]).abs().max()) <= 2e-2
+
+
+def test_nan_in_a_cache_row_stays_in_its_stream():
+    """A NaN key inside one stream's valid range poisons that stream only; the
+    other streams are bit-identical to a clean run."""
+    import parallax_local_linear_amd as plx
+    inp = wl.decode_inputs(2, 2, 300, 128, "bf16", seed=621, device="cuda", seqlens=[300, 200])
+    clean = plx.decode(inp["q"], inp["kcache"], inp["vcache"], inp["rho"], inp["gate"],
+                       inp["seqlens"], split_keys=128)
+    kc = inp["kcache"].clone()
+    kc[1, 0, 150, 3] = float("nan")
+    out = plx.decode(inp["q"], kc, inp["vcache"], inp["rho"], inp["gate"], inp["seqlens"],
+                     split_keys=128)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(out[1, 0]).all())
+    for b, h in [(0, 0), (0, 1), (1, 1)]:
+        assert torch.equal(out[b, h], clean[b, h])
