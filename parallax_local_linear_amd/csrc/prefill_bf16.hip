@@ -186,11 +186,12 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     voff[i] = (uint32_t)((r * PF_BC + ((pc ^ (r & 7)) << 3)) * 2);
   }
   const char* kbase = reinterpret_cast<const char*>(k + head);
-  auto load_k = [&](int kt, int buf) {
+  // blocks [i0, i1) of this wave's share of a K tile
+  auto load_k = [&](int kt, int buf, auto i0, auto i1) {
     const int rows = min(PF_BC, L - kt * PF_BC);
     const char* tile = kbase + (size_t)kt * PF_BC * D * 2;
 #pragma unroll
-    for (int i = 0; i < KBLK / NW; ++i)
+    for (int i = decltype(i0)::value; i < decltype(i1)::value; ++i)
       buffer_load_lds16(tile, rows * D * 2, smem + buf * LY::K_ELEMS + (i * NW + wave_u) * 512,
                         koff[i]);
   };
@@ -233,9 +234,12 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // while K of tile kt+2 and V of tile kt+1 are written into the buffers read in
   // iteration kt-1.  Plain schedule: iteration kt reads K and V of tile kt and
   // writes tile kt+1 into the other buffers.
-  load_k(0, 0);
+  using KAll0 = std::integral_constant<int, 0>;
+  using KHalf = std::integral_constant<int, KBLK / NW / 2>;
+  using KAll1 = std::integral_constant<int, KBLK / NW>;
+  load_k(0, 0, KAll0{}, KAll1{});
   load_v(0, 0);
-  if (PIPE && n_kt > 1) load_k(1, 1);
+  if (PIPE && n_kt > 1) load_k(1, 1, KAll0{}, KAll1{});
   wait_loads();
   __syncthreads();
 
@@ -324,9 +328,10 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
                        f32x4 (&ns)[4], f32x4 (&nr)[4]) -> float {
     constexpr int P = decltype(par)::value;
     scores(std::integral_constant<int, 1 - P>{}, ns, nr);
-    // The V tile of the next step is staged here rather than at the top of the
-    // iteration: the wave's vector-memory issue then overlaps its score MFMAs
-    // instead of delaying them.
+    // The second half of the K tile two steps ahead and the V tile of the next
+    // step are staged here rather than at the top of the iteration: the wave's
+    // vector-memory issue then overlaps its score MFMAs instead of delaying them.
+    load_k(min(kt_ + 2, n_kt - 1), P, KHalf{}, KAll1{});
     load_v(min(kt_ + 1, n_kt - 1), 1 - P);
     softmax_pv(par, cs, cr);
     return tile_max(ns, kt_ + 1, diag_next);
@@ -349,9 +354,13 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     // Staging is unconditional: past the last tile the loads re-read tile
     // n_kt-1 into buffers no wave reads again.
     const int k_ahead = PIPE ? kt + 2 : kt + 1;
-    load_k(min(k_ahead, n_kt - 1), PIPE ? P : 1 - P);
-    const bool v_in_step = PIPE && kt + 1 < n_w;     // pipe_step stages V itself
-    if (!v_in_step) load_v(min(kt + 1, n_kt - 1), 1 - P);
+    const bool in_step = PIPE && kt + 1 < n_w;     // pipe_step stages the rest itself
+    if (in_step) {
+      load_k(min(k_ahead, n_kt - 1), P, KAll0{}, KHalf{});
+    } else {
+      load_k(min(k_ahead, n_kt - 1), PIPE ? P : 1 - P, KAll0{}, KAll1{});
+      load_v(min(kt + 1, n_kt - 1), 1 - P);
+    }
     if (kt < n_w) {
       if constexpr (PIPE) {
         if (kt + 1 < n_w) {
