@@ -23,8 +23,10 @@
 //   * P = exp2(S*scale*log2e - m) and T = P*R are rounded to fp16 (RNE) and fed,
 //     as B operands, to v_mfma_f32_16x16x32_f16 against the V^T fragment:
 //     O^T += V^T P^T and A_r^T += V^T T^T, fp32 accumulators in registers.  The
-//     row sums l = sum P and c = sum T are taken from the same rounded values
-//     (v_dot2_f32_f16 against (1,1)), so a single key reproduces v exactly.
+//     row sums l = sum P and c = sum T come from the same rounded values, by one
+//     more MFMA each against an all-ones A block (every row of that product holds
+//     the per-query sums), so a single key reproduces v exactly and the vector
+//     ALU, the scarcer resource here, is spared 16 instructions per tile.
 //   * stage_v stores the keys of every 32-key group of V^T in the order in which
 //     the score accumulators of a lane group come out of two consecutive 16-key
 //     blocks, so P and T go from the score MFMA output straight into the value
@@ -152,7 +154,14 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     acc_o[fb] = f32x4{};
     acc_r[fb] = f32x4{};
   }
-  float m_run = kMinit, l_run = 0.f, c_run = 0.f;
+  float m_run = kMinit;
+  // l = sum_j P_ij and c = sum_j T_ij, accumulated on the matrix cores: the
+  // product of an all-ones 16x32 block with P^T (or T^T) holds the per-query
+  // sums in every row, so each lane's four values are copies of its query's.
+  f32x4 acc_l = {}, acc_c = {};
+  f16x8 ones8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones8[e] = (_Float16)1.0f;
 
   const int last_q = min(q0 + PF_BR, L) - 1;
   const int n_kt = last_q / PF_BC + 1;
@@ -225,7 +234,6 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     }
   };
 
-  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
   // tiles this wave computes: 0 .. n_w-1 (a row always sees key 0 of tile 0)
   const int n_w = (qw0 < L) ? wave_last_q / PF_BC + 1 : 0;
 
@@ -275,8 +283,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
-      l_run *= alpha;
-      c_run *= alpha;
+      acc_l *= alpha;
+      acc_c *= alpha;
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
         acc_o[fb] *= alpha;
@@ -302,13 +310,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
           tf[4 * hh + j] = (_Float16)tv;
         }
       }
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const f16x2 pp = {pf[2 * e2], pf[2 * e2 + 1]};
-        const f16x2 tt = {tf[2 * e2], tf[2 * e2 + 1]};
-        l_run = __builtin_amdgcn_fdot2(pp, ones, l_run, false);
-        c_run = __builtin_amdgcn_fdot2(tt, ones, c_run, false);
-      }
+      acc_l = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8, pf, acc_l, 0, 0, 0);
+      acc_c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8, tf, acc_c, 0, 0, 0);
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
         const f16x8 va =
@@ -389,8 +392,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   }
 
   // epilogue: o = o_sa - g (u - o_sa * rbar), o_sa = O/l, u = A_r/l, rbar = c/l
-  const float l_tot = lane_xor32(lane_xor16(l_run, Sum{}), Sum{});
-  const float c_tot = lane_xor32(lane_xor16(c_run, Sum{}), Sum{});
+  const float l_tot = acc_l[0];
+  const float c_tot = acc_c[0];
   if (qi < L) {
     const float inv = 1.0f / l_tot;
     const float rbar = c_tot * inv;
