@@ -18,8 +18,8 @@
 //     fragment read from LDS feeds both MFMAs (the joint QK / RK product).  Q
 //     and rho fragments stay in registers.
 //   * In the transposed layout a lane owns one query and 4 keys per block, so
-//     the online-softmax row reductions are lane-local except for two exchanges
-//     across the four lanes that share a query.
+//     the online-softmax row max is lane-local except for two exchanges across
+//     the four lanes that share a query.
 //   * P = exp2(S*scale*log2e - m) and T = P*R are rounded to fp16 (RNE) and fed,
 //     as B operands, to v_mfma_f32_16x16x32_f16 against the V^T fragment:
 //     O^T += V^T P^T and A_r^T += V^T T^T, fp32 accumulators in registers.  The
@@ -167,19 +167,18 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   const int n_kt = last_q / PF_BC + 1;
   const int wave_last_q = min(qw0 + 15, L - 1);
 
-  // Tiles move HBM -> LDS with global_load_lds_dwordx4: each lane's 16 bytes
-  // land at (wave-uniform base) + 16 * lane, so one wave instruction fills 1 KB
-  // of LDS; the lane's global address picks which logical chunk goes there,
-  // which implements the XOR swizzle without touching registers.
+  // Tiles move HBM -> LDS with buffer_load_dwordx4 ... lds: each lane's 16
+  // bytes land at (wave-uniform base) + 16 * lane, so one wave instruction
+  // fills 1 KB of LDS; the lane's offset into the tile picks which logical
+  // chunk goes there, which implements the XOR swizzle without touching
+  // registers.  The per-lane byte offsets of this wave's 1-KB blocks (swizzle
+  // included) are the same for every tile: computed once, one 32-bit register
+  // each.  Each load takes a scalar buffer descriptor based at the tile and
+  // sized to the bytes that exist, so K rows past L come back as zeros from
+  // the hardware range check (they only meet masked, future keys).
   constexpr int KBLK = LY::K_ELEMS * 2 / 1024;   // 1-KB blocks per K tile
   constexpr int VBLK = LY::V_ELEMS * 2 / 1024;   // 1-KB blocks per V^T tile
   static_assert(KBLK % NW == 0 && VBLK % NW == 0, "tile blocks per wave");
-  // Tiles move with buffer_load_dwordx4 ... lds.  The per-lane byte offsets of
-  // this wave's 1-KB blocks inside a tile (swizzle included) are the same for
-  // every tile: computed once, one 32-bit register each.  Each load takes a
-  // scalar buffer descriptor based at the tile and sized to the bytes that
-  // exist, so K rows past L come back as zeros from the hardware range check
-  // (they only meet masked, future keys).
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   uint32_t koff[KBLK / NW], voff[VBLK / NW];
 #pragma unroll
