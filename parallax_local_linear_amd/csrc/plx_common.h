@@ -66,9 +66,6 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, int bytes, v
 struct Max {
   __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
 };
-struct Sum {
-  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
-};
 
 // op(x[lane], x[lane ^ 16]) and op(x[lane], x[lane ^ 32]) for a commutative op.
 // With PLX_PERMLANE_SWAP the exchange uses gfx950's v_permlane{16,32}_swap (a
