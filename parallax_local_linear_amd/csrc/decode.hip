@@ -28,7 +28,7 @@ struct DecCfg {
   static constexpr int EPL = 16 / (int)sizeof(T);   // elements per lane per row load
   static constexpr int LPR = D / EPL;                // lanes per key row
   static constexpr int KPW = 64 / LPR;               // rows per wave load
-  static constexpr int U = 8;                        // row loads in flight per lane
+  static constexpr int U = 16;                       // row loads in flight per lane
   static constexpr int CHUNK = KPW * U;              // keys per wave iteration
   static constexpr int NG = 4 * KPW;                 // lane groups per workgroup
 };
