@@ -161,3 +161,23 @@ def test_full_workload_sampled(wid):
         worst = max(worst, err)
     print(f"workload {wid}: worst max-abs {worst:.3e}", flush=True)
     assert worst <= TOL["bf16"]
+
+
+def test_workload2_every_head():
+    """The benchmark's prefill workload (B4 H16 L4096 d128, bf16) compared with the
+    expanded-form oracle on every output element of all 64 heads."""
+    w = wl.WORKLOADS[2]
+    inp = wl.make_workload(2, device="cuda")
+    out = _plx().prefill(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"])
+    torch.cuda.synchronize()
+    got = _host(out).double().numpy()
+    h = {k: _host(inp[k]).double().numpy() for k in ("q", "k", "v", "rho", "gate")}
+    worst = 0.0
+    for b in range(w.B):
+        for hh in range(w.H):
+            ref = po.prefill_head(h["q"][b, hh], h["k"][b, hh], h["v"][b, hh], h["rho"][b, hh],
+                                  float(h["gate"][hh]), w.scale)
+            worst = max(worst, _maxerr(got[b, hh], ref))
+        print(f"workload 2: {(b + 1) * w.H} of {w.B * w.H} heads, worst max-abs {worst:.3e}",
+              flush=True)
+    assert worst <= TOL["bf16"]
