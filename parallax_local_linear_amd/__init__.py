@@ -35,6 +35,20 @@ def _stream(dev):
     return torch.cuda.current_stream(dev).cuda_stream
 
 
+def _launch(dev, name, *args):
+    """Call the library with `dev` as the current device: the kernels run on that
+    device's current torch stream (the last argument of every launching call)."""
+    with torch.cuda.device(dev):
+        return call(name, *args, _stream(dev))
+
+
+def _split(split_keys):
+    c = int(split_keys)
+    if c <= 0 or c % 64:
+        raise ValueError(f"split_keys must be a positive multiple of 64, got {split_keys}")
+    return c
+
+
 def _check(name, t, dtype=None, shape=None, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
@@ -89,14 +103,16 @@ def prefill(q, k, v, rho, gate, scale=None, out=None, workspace=None):
     elif workspace is not None:
         _check("workspace", workspace, device=q.device)
         wsb = workspace.numel() * workspace.element_size()
-    call("parallax_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(rho), _ptr(gate), _ptr(out),
-         B, H, L, d, _scale(scale, d), _DT[dt], _ptr(workspace), wsb, _stream(q.device))
+    _launch(q.device, "parallax_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(rho), _ptr(gate),
+            _ptr(out), B, H, L, d, _scale(scale, d), _DT[dt], _ptr(workspace), wsb)
     return out
 
 
 def prefill_stage_v(v, vt=None):
     """First stage of a bf16 prefill: V -> fp16 V^T tiles (a uint8 buffer)."""
     _check("v", v, torch.bfloat16)
+    if v.dim() != 4:
+        raise ValueError("v must be [B, H, L, d]")
     B, H, L, d = v.shape
     n = prefill_workspace_bytes(B, H, L, d, torch.bfloat16)
     if vt is None:
@@ -104,13 +120,15 @@ def prefill_stage_v(v, vt=None):
     _check("vt", vt, device=v.device)
     if vt.numel() * vt.element_size() < n:
         raise ValueError(f"vt must hold {n} bytes")
-    call("parallax_prefill_stage_v", _ptr(v), _ptr(vt), B, H, L, d, _stream(v.device))
+    _launch(v.device, "parallax_prefill_stage_v", _ptr(v), _ptr(vt), B, H, L, d)
     return vt
 
 
 def prefill_attend(q, k, vt, rho, gate, scale=None, out=None):
     """Second stage of a bf16 prefill, reading V from prefill_stage_v's buffer."""
     _check("q", q, torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, L, d]")
     B, H, L, d = q.shape
     for n, t in (("k", k), ("rho", rho)):
         _check(n, t, torch.bfloat16, q.shape, q.device)
@@ -121,8 +139,8 @@ def prefill_attend(q, k, vt, rho, gate, scale=None, out=None):
     if out is None:
         out = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
     _check("out", out, torch.float32, (B, H, L, d), q.device)
-    call("parallax_prefill_attend", _ptr(q), _ptr(k), _ptr(vt), _ptr(rho), _ptr(gate),
-         _ptr(out), B, H, L, d, _scale(scale, d), _stream(q.device))
+    _launch(q.device, "parallax_prefill_attend", _ptr(q), _ptr(k), _ptr(vt), _ptr(rho),
+            _ptr(gate), _ptr(out), B, H, L, d, _scale(scale, d))
     return out
 
 
@@ -157,28 +175,32 @@ def decode(q, kcache, vcache, rho, gate, seqlens, scale=None, split_keys=0, out=
         workspace = torch.empty(max(wsb, 4), dtype=torch.uint8, device=q.device)
     _check("workspace", workspace, device=q.device)
     wsb = workspace.numel() * workspace.element_size()
-    call("parallax_decode", _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(rho), _ptr(gate),
-         _ptr(out), _ptr(seqlens), B, H, Lmax, d, _scale(scale, d), _DT[dt], int(split_keys),
-         _ptr(workspace), wsb, _stream(q.device))
+    _launch(q.device, "parallax_decode", _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(rho),
+            _ptr(gate), _ptr(out), _ptr(seqlens), B, H, Lmax, d, _scale(scale, d), _DT[dt],
+            int(split_keys), _ptr(workspace), wsb)
     return out
 
 
 def decode_partials(q, kcache, vcache, rho, seqlens, split_keys, scale=None, partials=None):
     """First stage of decode: per-split partial records [B, H, S, 2d+4] fp32."""
     B, H, Lmax, d, dt = _decode_checks(q, kcache, vcache, rho, seqlens)
+    split_keys = _split(split_keys)
     S = -(-Lmax // split_keys)
     if partials is None:
         partials = torch.empty((B, H, S, 2 * d + 4), dtype=torch.float32, device=q.device)
     _check("partials", partials, torch.float32, (B, H, S, 2 * d + 4), q.device)
-    call("parallax_decode_partials", _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(rho),
-         _ptr(seqlens), _ptr(partials), B, H, Lmax, d, _scale(scale, d), _DT[dt],
-         int(split_keys), _stream(q.device))
+    _launch(q.device, "parallax_decode_partials", _ptr(q), _ptr(kcache), _ptr(vcache),
+            _ptr(rho), _ptr(seqlens), _ptr(partials), B, H, Lmax, d, _scale(scale, d),
+            _DT[dt], split_keys)
     return partials
 
 
 def decode_combine(partials, gate, seqlens, Lmax, split_keys, out=None):
     """Second stage of decode: merge the partial records into out [B, H, d]."""
     _check("partials", partials, torch.float32)
+    if partials.dim() != 4:
+        raise ValueError("partials must be [B, H, S, 2d+4]")
+    split_keys = _split(split_keys)
     B, H, S, w = partials.shape
     d = (w - 4) // 2
     _check("gate", gate, torch.float32, (H,), partials.device)
@@ -188,6 +210,6 @@ def decode_combine(partials, gate, seqlens, Lmax, split_keys, out=None):
     if out is None:
         out = torch.empty((B, H, d), dtype=torch.float32, device=partials.device)
     _check("out", out, torch.float32, (B, H, d), partials.device)
-    call("parallax_decode_combine", _ptr(partials), _ptr(gate), _ptr(seqlens), _ptr(out), B, H,
-         Lmax, d, int(split_keys), _stream(partials.device))
+    _launch(partials.device, "parallax_decode_combine", _ptr(partials), _ptr(gate),
+            _ptr(seqlens), _ptr(out), B, H, Lmax, d, split_keys)
     return out

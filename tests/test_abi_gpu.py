@@ -69,3 +69,26 @@ def test_decode_seqlens_clamped_on_device():
     got = out.cpu().double().numpy()
     assert np.all(got[1] == 0.0)
     assert float(np.max(np.abs(got - ref))) <= 2e-2
+
+
+def test_binding_rejects_bad_arguments():
+    """The torch binding refuses mismatched tensors before calling the library."""
+    import parallax_local_linear_amd as plx
+    inp = wl.prefill_inputs(1, 2, 64, 64, "bf16", seed=34, device="cuda")
+    with pytest.raises(ValueError):
+        plx.prefill(inp["q"], inp["k"][:, :, :32].contiguous(), inp["v"], inp["rho"], inp["gate"])
+    with pytest.raises(TypeError):
+        plx.prefill(inp["q"], inp["k"].float(), inp["v"], inp["rho"], inp["gate"])
+    with pytest.raises(ValueError):
+        plx.prefill(inp["q"], inp["k"].transpose(2, 3), inp["v"], inp["rho"], inp["gate"])
+    with pytest.raises(ValueError):
+        plx.prefill_stage_v(inp["v"][0])
+    dec = wl.decode_inputs(2, 2, 128, 64, "bf16", seed=35, device="cuda")
+    for bad in (0, 100, -64):
+        with pytest.raises(ValueError):
+            plx.decode_partials(dec["q"], dec["kcache"], dec["vcache"], dec["rho"],
+                                dec["seqlens"], bad)
+    with pytest.raises(plx.ParallaxError):
+        plx.decode(dec["q"], dec["kcache"], dec["vcache"], dec["rho"], dec["gate"],
+                   dec["seqlens"], split_keys=100)
+    torch.cuda.synchronize()

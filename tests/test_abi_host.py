@@ -101,3 +101,14 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_native, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(ImportError):
         _native.lib()
+
+
+def test_binding_requires_gpu_tensors():
+    """Host tensors are refused by the binding before the library is touched."""
+    import torch
+    import parallax_local_linear_amd as plx
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        plx.prefill(x, x, x, x, torch.ones(1))
+    with pytest.raises(ValueError, match="GPU"):
+        plx.decode(x[:, :, 0], x, x, x[:, :, 0], torch.ones(1), torch.ones(1, dtype=torch.int32))
