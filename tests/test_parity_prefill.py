@@ -181,3 +181,20 @@ def test_workload2_every_head():
         print(f"workload 2: {(b + 1) * w.H} of {w.B * w.H} heads, worst max-abs {worst:.3e}",
               flush=True)
     assert worst <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_long_sequence_sampled(d):
+    """A single long head (L = 65537, one past a power of two): sampled rows,
+    including the last ones, against the explicit-form oracle."""
+    L = 65537
+    inp = wl.prefill_inputs(1, 1, L, d, "bf16", seed=700 + d, device="cuda", rho_std=0.5,
+                            gate=("uniform", 0.2, 1.0))
+    out = _plx().prefill(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"])
+    torch.cuda.synchronize()
+    h = {k: _host(v) for k, v in inp.items()}
+    rows = [0, 1, 4095, 4096, 32768, 65535, 65536]
+    ref = po.prefill_rows(h["q"], h["k"], h["v"], h["rho"], h["gate"], 0, 0, rows)
+    err = _maxerr(_host(out[0, 0, rows]).double().numpy(), ref)
+    print(f"L={L} d={d}: max-abs {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
