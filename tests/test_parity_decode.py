@@ -131,3 +131,20 @@ def test_workload4_sampled():
     print(f"workload 4 ({len(streams)} streams): max-abs {err:.3e}", flush=True)
     assert err <= TOL["bf16"]
     assert np.isfinite(out).all()
+
+
+def test_widest_grid():
+    """B*H = 65535 streams, the largest second grid dimension the decode launch
+    uses; sampled streams against the oracle."""
+    B, H, Lmax, d = 65535, 1, 64, 64
+    rng = np.random.default_rng(36)
+    sl = rng.integers(0, Lmax + 1, B).tolist()
+    inp = wl.decode_inputs(B, H, Lmax, d, "bf16", seed=36, device="cuda", seqlens=sl)
+    out = _host(_run(inp)).double().numpy()
+    streams = [0, 1, 2, 32767, 65533, 65534]
+    h = {k: _host(v) for k, v in inp.items()}
+    ref = po.decode(h["q"], h["kcache"], h["vcache"], h["rho"], h["gate"], h["seqlens"],
+                    streams=[(b, 0) for b in streams])
+    err = max(_maxerr(out[b, 0], ref[b, 0]) for b in streams)
+    print(f"decode B*H=65535: max-abs over sampled streams {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]

@@ -198,3 +198,21 @@ def test_long_sequence_sampled(d):
     err = _maxerr(_host(out[0, 0, rows]).double().numpy(), ref)
     print(f"L={L} d={d}: max-abs {err:.3e}", flush=True)
     assert err <= TOL["bf16"]
+
+
+def test_many_heads():
+    """B*H = 4096 short heads: the grid's head index runs over thousands of heads."""
+    B, H, L, d = 64, 64, 100, 64
+    inp = wl.prefill_inputs(B, H, L, d, "bf16", seed=710, device="cuda", rho_std=0.5,
+                            gate=("uniform", 0.2, 1.0))
+    out = _plx().prefill(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"])
+    torch.cuda.synchronize()
+    h = {k: _host(v) for k, v in inp.items()}
+    worst = 0.0
+    for b, hh in [(0, 0), (0, 63), (31, 17), (63, 63)]:
+        ref = po.prefill_head(h["q"][b, hh].double().numpy(), h["k"][b, hh].double().numpy(),
+                              h["v"][b, hh].double().numpy(), h["rho"][b, hh].double().numpy(),
+                              float(h["gate"][hh]), 1.0 / 8.0)
+        worst = max(worst, _maxerr(_host(out[b, hh]).double().numpy(), ref))
+    print(f"prefill B*H=4096: max-abs {worst:.3e}", flush=True)
+    assert worst <= TOL["bf16"]
