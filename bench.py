@@ -35,9 +35,11 @@ METRIC = ("Parallax decode HBM GB/s (% of peak) + prefill TFLOP/s (% bf16 MFMA p
 PEAK_MFMA_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0               # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = {
-    "prefill_bf16_kernel": "parallax_local_linear_amd/csrc/prefill_bf16.hip",
-    "decode_split_kernel": "parallax_local_linear_amd/csrc/decode.hip",
+KERNEL_SOURCES = {   # the files whose text determines each kernel's code
+    "prefill_bf16_kernel": ["parallax_local_linear_amd/csrc/prefill_bf16.hip",
+                            "parallax_local_linear_amd/csrc/plx_common.h"],
+    "decode_split_kernel": ["parallax_local_linear_amd/csrc/decode.hip",
+                            "parallax_local_linear_amd/csrc/plx_common.h"],
 }
 
 
@@ -46,8 +48,11 @@ def log(*a):
 
 
 def src_sha(kernel):
-    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic(kernel):
