@@ -16,6 +16,9 @@ decode block carries its own for the split-KV kernel.
 
 Unless --no-extra is given, the two other full-size workloads (long ragged
 decode and the d=64 prefill) are timed too and reported under "extra".
+"softmax_relative" times the same kernels with the correction branch compiled
+out (plain causal softmax attention) against the Parallax kernels on each
+workload, alternating the two launch by launch, and reports the time ratio.
 The CPU baseline times the fp64 oracle on a bounded sample on the host.
 Prints exactly one JSON line on stdout.
 """
@@ -159,6 +162,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true", help="skip workloads 4 and 5")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-softmax", action="store_true",
+                    help="skip the timing against the softmax-only kernels")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size kernel for scaling HBM byte counters)")
@@ -269,8 +274,17 @@ def main():
         res["calib_copy_bytes"] = {"read": n * 4, "write": n * 4}
         del src, dst
 
+    rel = []
+    if not args.no_softmax:
+        log("softmax-relative timing: workloads 2 and 3")
+        rel.append(softmax_relative_prefill(torch, plx, wl, pin, wp, vt, pout))
+        rel.append(softmax_relative_decode(torch, plx, wl, din, wd))
     if not args.no_extra:
-        res["extra"] = extra_workloads(torch, plx, wl, dev)
+        res["extra"], rel_extra = extra_workloads(torch, plx, wl, dev,
+                                                  softmax=not args.no_softmax)
+        rel += rel_extra
+    if rel:
+        res["softmax_relative"] = rel
 
     if not args.no_cpu:
         log("cpu baseline")
@@ -279,9 +293,58 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def extra_workloads(torch, plx, wl, dev, steps=10):
+def softmax_relative_prefill(torch, plx, wl, inp, w, vt, pout, steps=10):
+    """Parallax prefill against the same kernels with the correction compiled out,
+    on one workload.  The V staging pass is the same for both and is timed once
+    per step; the attend kernels alternate launch by launch."""
+    tm = Timer(torch)
+    for _ in range(steps + 2):
+        tm.run("stage_v", lambda: plx.prefill_stage_v(inp["v"], vt))
+        tm.run("parallax", lambda: plx.prefill_attend(inp["q"], inp["k"], vt, inp["rho"],
+                                                      inp["gate"], out=pout))
+        tm.run("softmax", lambda: plx.softmax_prefill_attend(inp["q"], inp["k"], vt, out=pout))
+    torch.cuda.synchronize()
+    st, pa, sm = tm.ms("stage_v", 2), tm.ms("parallax", 2), tm.ms("softmax", 2)
+    fl = wl.prefill_flops(w.B, w.H, w.L, w.d)
+    return {"workload": w.name, "kind": "prefill",
+            "parallax_attend_ms": round(pa, 4), "softmax_attend_ms": round(sm, 4),
+            "attend_time_ratio": round(pa / sm, 4),
+            "stage_v_ms": round(st, 4), "path_time_ratio": round((st + pa) / (st + sm), 4),
+            "parallax_attend_TFLOP/s": round(fl / pa / 1e9, 2),
+            "softmax_attend_TFLOP/s": round(fl / 2 / sm / 1e9, 2),
+            "flops": {"parallax": fl, "softmax": fl / 2}}
+
+
+def softmax_relative_decode(torch, plx, wl, inp, w, steps=10):
+    """Parallax decode step against the softmax-only decode step (split pass and
+    combine each, same split size and workspace), alternating launch by launch."""
+    B, H, Lmax, d = w.B, w.H, w.Lmax, w.d
+    C = plx.decode_default_split(B, H, Lmax, d)
+    ws = torch.empty(plx.decode_workspace_bytes(B, H, Lmax, d, C), dtype=torch.uint8,
+                     device=inp["q"].device)
+    out = torch.empty((B, H, d), dtype=torch.float32, device=inp["q"].device)
+    tm = Timer(torch)
+    for _ in range(steps + 2):
+        tm.run("parallax", lambda: plx.decode(inp["q"], inp["kcache"], inp["vcache"], inp["rho"],
+                                              inp["gate"], inp["seqlens"], split_keys=C,
+                                              out=out, workspace=ws))
+        tm.run("softmax", lambda: plx.softmax_decode(inp["q"], inp["kcache"], inp["vcache"],
+                                                     inp["seqlens"], split_keys=C, out=out,
+                                                     workspace=ws))
+    torch.cuda.synchronize()
+    pa, sm = tm.ms("parallax", 2), tm.ms("softmax", 2)
+    nb = wl.decode_bytes(inp["seqlens"].tolist(), H, d)
+    nb_sm = nb - B * H * d * 2 - 4 * H          # no rho, no gate
+    return {"workload": w.name, "kind": "decode", "split_keys": C,
+            "parallax_ms": round(pa, 4), "softmax_ms": round(sm, 4),
+            "time_ratio": round(pa / sm, 4),
+            "parallax_GB/s": round(nb / pa / 1e6, 1), "softmax_GB/s": round(nb_sm / sm / 1e6, 1),
+            "bytes": {"parallax": nb, "softmax": nb_sm}}
+
+
+def extra_workloads(torch, plx, wl, dev, steps=10, softmax=True):
     """Long ragged decode (B8 H16, 65536..131072 keys) and the d=64 prefill."""
-    out = []
+    out, rel = [], []
     w4 = wl.WORKLOADS[4]
     log("extra: decode workload 4")
     din = wl.make_workload(4, device=dev)
@@ -302,7 +365,11 @@ def extra_workloads(torch, plx, wl, dev, steps=10):
     out.append({"workload": w4.name, "ms": round(ms, 4), "GB/s": round(nb / ms / 1e6, 1),
                 "frac_of_hbm_peak": round(nb / ms / 1e6 / PEAK_HBM_GBS, 4), "bytes": nb,
                 "seqlens": din["seqlens"].tolist(), "split_keys": C})
-    del din, part, dout
+    del part, dout
+    if softmax:
+        log("softmax-relative timing: workload 4")
+        rel.append(softmax_relative_decode(torch, plx, wl, din, w4))
+    del din
     torch.cuda.empty_cache()
 
     w5 = wl.WORKLOADS[5]
@@ -325,9 +392,12 @@ def extra_workloads(torch, plx, wl, dev, steps=10):
                 "frac_of_mfma_peak": round(fl / ms / 1e9 / PEAK_MFMA_BF16_TFLOPS, 4),
                 "attend_ms": round(ms_a, 4),
                 "attend_TFLOP/s": round(fl / ms_a / 1e9, 2), "flops": fl})
+    if softmax:
+        log("softmax-relative timing: workload 5")
+        rel.append(softmax_relative_prefill(torch, plx, wl, pin, w5, vt, pout))
     del pin, vt, pout
     torch.cuda.empty_cache()
-    return out
+    return out, rel
 
 
 if __name__ == "__main__":

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 1
+#define PARALLAX_ABI_VERSION 2
 
 typedef enum {
   PLX_OK = 0,
@@ -147,6 +147,37 @@ int parallax_decode_combine(const float* partials, const float* gate, const int3
 
 /* The split size parallax_decode uses when split_keys is 0. */
 int parallax_decode_default_split(int B, int H, int Lmax, int d);
+
+/* --------------------------------------------------------- softmax baseline
+ * Plain causal softmax attention, o_i = o^SA_i (Eq. 2 without the correction
+ * branch), computed by the same kernels as the Parallax calls above with the
+ * covariance branch removed at compile time: same staging, tiling, launch
+ * shapes and precision, no rho reads, no <rho,k> products, no r-weighted
+ * accumulators.  The page's efficiency claim (section "Key contributions")
+ * compares Parallax kernels with softmax-attention kernels over batch sizes and
+ * context lengths, and section "Hardware-aware algorithm" puts the extra work
+ * at about twice the compute over a shared KV stream; these entry points are
+ * the like-for-like softmax side of that comparison on this hardware.
+ * Arguments, layouts, workspaces and error rules are those of the matching
+ * Parallax call with rho and gate left out:
+ *   parallax_softmax_prefill        <-> parallax_prefill
+ *                                       (workspace: parallax_prefill_workspace_bytes)
+ *   parallax_softmax_prefill_attend <-> parallax_prefill_attend
+ *                                       (vt16 from parallax_prefill_stage_v)
+ *   parallax_softmax_decode         <-> parallax_decode
+ *                                       (workspace: parallax_decode_workspace_bytes,
+ *                                        which also covers this call's smaller records) */
+int parallax_softmax_prefill(const void* q, const void* k, const void* v, float* out,
+                             int B, int H, int L, int d, float scale, int dtype,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+int parallax_softmax_prefill_attend(const void* q, const void* k, const void* vt16, float* out,
+                                    int B, int H, int L, int d, float scale, void* stream);
+
+int parallax_softmax_decode(const void* q, const void* kcache, const void* vcache, float* out,
+                            const int32_t* seqlens, int B, int H, int Lmax, int d, float scale,
+                            int dtype, int split_keys, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 #ifdef __cplusplus
 }

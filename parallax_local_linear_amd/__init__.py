@@ -8,9 +8,11 @@ Language Modeling", section "Core mechanism", Eq. 2) is
 softmax attention minus a gated correction: the softmax-weighted covariance of
 values and keys applied to the probe rho_i.  `prefill` runs the causal forward
 pass over whole sequences; `decode` runs one query per sequence against a KV
-cache.  Both are thin wrappers over the C ABI of libparallax.so: they check
-shapes, allocate outputs and workspaces with torch on the inputs' device, and
-enqueue the HIP kernels on torch's current stream.
+cache.  The `softmax_*` functions run the same kernels with the correction
+branch compiled out (plain causal softmax attention), the like-for-like
+baseline for the cost of the correction.  All are thin wrappers over the C ABI
+of libparallax.so: they check shapes, allocate outputs and workspaces with torch
+on the inputs' device, and enqueue the HIP kernels on torch's current stream.
 """
 from __future__ import annotations
 
@@ -22,7 +24,8 @@ from ._native import PLX_BF16, PLX_F32, ParallaxError, call, lib  # noqa: F401
 
 __all__ = ["prefill", "decode", "prefill_stage_v", "prefill_attend", "decode_partials",
            "decode_combine", "prefill_workspace_bytes", "decode_workspace_bytes",
-           "decode_default_split", "ParallaxError"]
+           "decode_default_split", "softmax_prefill", "softmax_prefill_attend",
+           "softmax_decode", "ParallaxError"]
 
 _DT = {torch.bfloat16: PLX_BF16, torch.float32: PLX_F32}
 
@@ -80,19 +83,21 @@ def decode_default_split(B, H, Lmax, d) -> int:
     return int(lib().parallax_decode_default_split(B, H, Lmax, d))
 
 
-def prefill(q, k, v, rho, gate, scale=None, out=None, workspace=None):
-    """Causal Parallax prefill.  q, k, v, rho: [B, H, L, d] bf16 or fp32 on one
-    GPU; gate: [H] fp32.  Returns out [B, H, L, d] fp32."""
+def _prefill_checks(q, others):
     _check("q", q)
     if q.dim() != 4:
         raise ValueError("q must be [B, H, L, d]")
-    B, H, L, d = q.shape
     dt = q.dtype
     if dt not in _DT:
         raise TypeError(f"unsupported dtype {dt}")
-    for n, t in (("k", k), ("v", v), ("rho", rho)):
+    for n, t in others:
         _check(n, t, dt, q.shape, q.device)
-    _check("gate", gate, torch.float32, (H,), q.device)
+    return (*q.shape, dt)
+
+
+def _prefill_out_ws(q, out, workspace):
+    B, H, L, d = q.shape
+    dt = q.dtype
     if out is None:
         out = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
     _check("out", out, torch.float32, (B, H, L, d), q.device)
@@ -103,8 +108,28 @@ def prefill(q, k, v, rho, gate, scale=None, out=None, workspace=None):
     elif workspace is not None:
         _check("workspace", workspace, device=q.device)
         wsb = workspace.numel() * workspace.element_size()
+    return out, workspace, wsb
+
+
+def prefill(q, k, v, rho, gate, scale=None, out=None, workspace=None):
+    """Causal Parallax prefill.  q, k, v, rho: [B, H, L, d] bf16 or fp32 on one
+    GPU; gate: [H] fp32.  Returns out [B, H, L, d] fp32."""
+    B, H, L, d, dt = _prefill_checks(q, (("k", k), ("v", v), ("rho", rho)))
+    _check("gate", gate, torch.float32, (H,), q.device)
+    out, workspace, wsb = _prefill_out_ws(q, out, workspace)
     _launch(q.device, "parallax_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(rho), _ptr(gate),
             _ptr(out), B, H, L, d, _scale(scale, d), _DT[dt], _ptr(workspace), wsb)
+    return out
+
+
+def softmax_prefill(q, k, v, scale=None, out=None, workspace=None):
+    """Causal softmax attention through the prefill kernels with the correction
+    branch compiled out.  q, k, v: [B, H, L, d] bf16 or fp32.  Returns out
+    [B, H, L, d] fp32."""
+    B, H, L, d, dt = _prefill_checks(q, (("k", k), ("v", v)))
+    out, workspace, wsb = _prefill_out_ws(q, out, workspace)
+    _launch(q.device, "parallax_softmax_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+            B, H, L, d, _scale(scale, d), _DT[dt], _ptr(workspace), wsb)
     return out
 
 
@@ -144,8 +169,28 @@ def prefill_attend(q, k, vt, rho, gate, scale=None, out=None):
     return out
 
 
+def softmax_prefill_attend(q, k, vt, scale=None, out=None):
+    """Softmax-only second stage of a bf16 prefill, reading V from
+    prefill_stage_v's buffer."""
+    _check("q", q, torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, L, d]")
+    B, H, L, d = q.shape
+    _check("k", k, torch.bfloat16, q.shape, q.device)
+    _check("vt", vt, device=q.device)
+    if vt.numel() * vt.element_size() < prefill_workspace_bytes(B, H, L, d):
+        raise ValueError("vt is too small")
+    if out is None:
+        out = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
+    _check("out", out, torch.float32, (B, H, L, d), q.device)
+    _launch(q.device, "parallax_softmax_prefill_attend", _ptr(q), _ptr(k), _ptr(vt), _ptr(out),
+            B, H, L, d, _scale(scale, d))
+    return out
+
+
 def _decode_checks(q, kcache, vcache, rho, seqlens):
     _check("q", q)
+    _check("kcache", kcache)
     if q.dim() != 3 or kcache.dim() != 4:
         raise ValueError("q must be [B, H, d] and kcache [B, H, Lmax, d]")
     B, H, d = q.shape
@@ -153,7 +198,8 @@ def _decode_checks(q, kcache, vcache, rho, seqlens):
     dt = q.dtype
     if dt not in _DT:
         raise TypeError(f"unsupported dtype {dt}")
-    _check("rho", rho, dt, (B, H, d), q.device)
+    if rho is not None:
+        _check("rho", rho, dt, (B, H, d), q.device)
     _check("kcache", kcache, dt, (B, H, Lmax, d), q.device)
     _check("vcache", vcache, dt, (B, H, Lmax, d), q.device)
     _check("seqlens", seqlens, torch.int32, (B,), q.device)
@@ -178,6 +224,26 @@ def decode(q, kcache, vcache, rho, gate, seqlens, scale=None, split_keys=0, out=
     _launch(q.device, "parallax_decode", _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(rho),
             _ptr(gate), _ptr(out), _ptr(seqlens), B, H, Lmax, d, _scale(scale, d), _DT[dt],
             int(split_keys), _ptr(workspace), wsb)
+    return out
+
+
+def softmax_decode(q, kcache, vcache, seqlens, scale=None, split_keys=0, out=None,
+                   workspace=None):
+    """One softmax-attention decode step through the decode kernels with the
+    correction branch compiled out.  Arguments as for decode, without rho and
+    gate.  Returns out [B, H, d] fp32."""
+    B, H, Lmax, d, dt = _decode_checks(q, kcache, vcache, None, seqlens)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    _check("out", out, torch.float32, (B, H, d), q.device)
+    if workspace is None:
+        wsb = decode_workspace_bytes(B, H, Lmax, d, split_keys)
+        workspace = torch.empty(max(wsb, 4), dtype=torch.uint8, device=q.device)
+    _check("workspace", workspace, device=q.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _launch(q.device, "parallax_softmax_decode", _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(out),
+            _ptr(seqlens), B, H, Lmax, d, _scale(scale, d), _DT[dt], int(split_keys),
+            _ptr(workspace), wsb)
     return out
 
 

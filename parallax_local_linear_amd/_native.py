@@ -34,6 +34,11 @@ SIGNATURES = {
                                       _i, _vp]),
     "parallax_decode_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "parallax_decode_default_split": (_i, [_i, _i, _i, _i]),
+    "parallax_softmax_prefill": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _sz,
+                                      _vp]),
+    "parallax_softmax_prefill_attend": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp]),
+    "parallax_softmax_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp,
+                                     _sz, _vp]),
 }
 
 _lib = None

@@ -12,17 +12,18 @@
 
 namespace plx {
 hipError_t launch_stage_v(const void* v, void* vt, int BH, int L, int d, hipStream_t s);
+// corr = false: the same kernels with the covariance branch compiled out
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* vt, const void* rho,
                                const float* gate, float* out, int B, int H, int L, int d,
-                               float scale, hipStream_t s);
+                               float scale, bool corr, hipStream_t s);
 hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, const void* rho,
                               const float* gate, float* out, int B, int H, int L, int d,
-                              float scale, hipStream_t s);
+                              float scale, bool corr, hipStream_t s);
 hipError_t launch_decode_split(const void* q, const void* kc, const void* vc, const void* rho,
                                const int* seqlens, float* part, int B, int H, int Lmax, int d,
-                               int C, float scale, bool bf16, hipStream_t s);
+                               int C, float scale, bool bf16, bool corr, hipStream_t s);
 hipError_t launch_decode_combine(const float* part, const float* gate, const int* seqlens,
-                                 float* out, int B, int H, int Lmax, int d, int C,
+                                 float* out, int B, int H, int Lmax, int d, int C, bool corr,
                                  hipStream_t s);
 }  // namespace plx
 
@@ -45,6 +46,10 @@ int ok() {
 
 int hip_fail(const char* what, hipError_t e) {
   return fail(PLX_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int launch_fail(const char* fn, const char* kernel, hipError_t e) {
+  return fail(PLX_EHIP, "%s: %s launch: %s", fn, kernel, hipGetErrorString(e));
 }
 
 constexpr int kTileKeys = 64;
@@ -124,6 +129,96 @@ struct Scratch {
   }
 };
 
+// The caller's workspace when it is large enough, else stream-ordered scratch.
+bool get_workspace(void* workspace, size_t workspace_bytes, size_t need, hipStream_t s,
+                   Scratch* scratch, void** ws, const char* fn, int* status) {
+  if (workspace) {
+    if (workspace_bytes < need) {
+      *status = fail(PLX_EINVAL, "%s: workspace of %zu bytes is smaller than the %zu required",
+                     fn, workspace_bytes, need);
+      return false;
+    }
+    *ws = workspace;
+    return true;
+  }
+  hipError_t e = hipMallocAsync(&scratch->ptr, need, s);
+  if (e != hipSuccess) {
+    *status = fail(PLX_ENOMEM, "%s: hipMallocAsync(%zu): %s", fn, need, hipGetErrorString(e));
+    return false;
+  }
+  scratch->stream = s;
+  *ws = scratch->ptr;
+  return true;
+}
+
+// Whole prefill; rho and gate are ignored (may be null) when corr is false.
+int prefill_impl(const char* fn, const void* q, const void* k, const void* v, const void* rho,
+                 const float* gate, float* out, int B, int H, int L, int d, float scale,
+                 int dtype, void* workspace, size_t workspace_bytes, hipStream_t s, bool corr) {
+  int st = PLX_OK;
+  if (!dims_ok(B, H, L, d, fn, "L", &st)) return st;
+  if (!dtype_ok(dtype, fn, &st)) return st;
+  if (!q || !k || !v || !out || (corr && (!rho || !gate)))
+    return fail(PLX_EINVAL, "%s: null pointer", fn);
+  const float sc = eff_scale(scale, d);
+  if (dtype == PLX_F32) {
+    hipError_t e = plx::launch_prefill_f32(q, k, v, rho, gate, out, B, H, L, d, sc, corr, s);
+    if (e != hipSuccess) return launch_fail(fn, "fp32 prefill", e);
+    return ok();
+  }
+  Scratch scratch;
+  void* ws = nullptr;
+  if (!get_workspace(workspace, workspace_bytes, vt_bytes(B, H, L, d), s, &scratch, &ws, fn,
+                     &st))
+    return st;
+  hipError_t e = plx::launch_stage_v(v, ws, B * H, L, d, s);
+  if (e != hipSuccess) return launch_fail(fn, "stage_v", e);
+  e = plx::launch_prefill_bf16(q, k, ws, rho, gate, out, B, H, L, d, sc, corr, s);
+  if (e != hipSuccess) return launch_fail(fn, "attend", e);
+  return ok();
+}
+
+int attend_impl(const char* fn, const void* q, const void* k, const void* vt16, const void* rho,
+                const float* gate, float* out, int B, int H, int L, int d, float scale,
+                hipStream_t s, bool corr) {
+  int st = PLX_OK;
+  if (!dims_ok(B, H, L, d, fn, "L", &st)) return st;
+  if (!q || !k || !vt16 || !out || (corr && (!rho || !gate)))
+    return fail(PLX_EINVAL, "%s: null pointer", fn);
+  hipError_t e = plx::launch_prefill_bf16(q, k, vt16, rho, gate, out, B, H, L, d,
+                                          eff_scale(scale, d), corr, s);
+  if (e != hipSuccess) return launch_fail(fn, "attend", e);
+  return ok();
+}
+
+// Whole decode step; rho and gate are ignored (may be null) when corr is false.
+int decode_impl(const char* fn, const void* q, const void* kcache, const void* vcache,
+                const void* rho, const float* gate, float* out, const int32_t* seqlens, int B,
+                int H, int Lmax, int d, float scale, int dtype, int split_keys, void* workspace,
+                size_t workspace_bytes, hipStream_t s, bool corr) {
+  int st = PLX_OK;
+  if (!dims_ok(B, H, Lmax, d, fn, "Lmax", &st)) return st;
+  if (!streams_ok(B, H, fn, &st)) return st;
+  if (!dtype_ok(dtype, fn, &st)) return st;
+  if (split_keys < 0) return fail(PLX_EINVAL, "%s: split_keys must be >= 0", fn);
+  const int C = split_keys > 0 ? split_keys : default_split(B, H, Lmax);
+  if (!split_ok(C, fn, &st)) return st;
+  if (!q || !kcache || !vcache || !out || !seqlens || (corr && (!rho || !gate)))
+    return fail(PLX_EINVAL, "%s: null pointer", fn);
+  Scratch scratch;
+  void* ws = nullptr;
+  if (!get_workspace(workspace, workspace_bytes, part_bytes(B, H, Lmax, d, C), s, &scratch, &ws,
+                     fn, &st))
+    return st;
+  float* part = static_cast<float*>(ws);
+  hipError_t e = plx::launch_decode_split(q, kcache, vcache, rho, seqlens, part, B, H, Lmax, d,
+                                          C, eff_scale(scale, d), dtype == PLX_BF16, corr, s);
+  if (e != hipSuccess) return launch_fail(fn, "split", e);
+  e = plx::launch_decode_combine(part, gate, seqlens, out, B, H, Lmax, d, C, corr, s);
+  if (e != hipSuccess) return launch_fail(fn, "combine", e);
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -150,50 +245,15 @@ int parallax_prefill_stage_v(const void* v, void* vt16, int B, int H, int L, int
 int parallax_prefill_attend(const void* q, const void* k, const void* vt16, const void* rho,
                             const float* gate, float* out, int B, int H, int L, int d,
                             float scale, void* stream) {
-  int st = PLX_OK;
-  if (!dims_ok(B, H, L, d, "parallax_prefill_attend", "L", &st)) return st;
-  if (!q || !k || !vt16 || !rho || !gate || !out)
-    return fail(PLX_EINVAL, "parallax_prefill_attend: null pointer");
-  hipError_t e = plx::launch_prefill_bf16(q, k, vt16, rho, gate, out, B, H, L, d,
-                                          eff_scale(scale, d), (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail("parallax_prefill_attend launch", e);
-  return ok();
+  return attend_impl("parallax_prefill_attend", q, k, vt16, rho, gate, out, B, H, L, d, scale,
+                     (hipStream_t)stream, true);
 }
 
 int parallax_prefill(const void* q, const void* k, const void* v, const void* rho,
                      const float* gate, float* out, int B, int H, int L, int d, float scale,
                      int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "parallax_prefill";
-  int st = PLX_OK;
-  if (!dims_ok(B, H, L, d, fn, "L", &st)) return st;
-  if (!dtype_ok(dtype, fn, &st)) return st;
-  if (!q || !k || !v || !rho || !gate || !out) return fail(PLX_EINVAL, "%s: null pointer", fn);
-  hipStream_t s = (hipStream_t)stream;
-  const float sc = eff_scale(scale, d);
-  if (dtype == PLX_F32) {
-    hipError_t e = plx::launch_prefill_f32(q, k, v, rho, gate, out, B, H, L, d, sc, s);
-    if (e != hipSuccess) return hip_fail("parallax_prefill launch", e);
-    return ok();
-  }
-  const size_t need = vt_bytes(B, H, L, d);
-  Scratch scratch;
-  void* ws = workspace;
-  if (ws) {
-    if (workspace_bytes < need)
-      return fail(PLX_EINVAL, "%s: workspace of %zu bytes is smaller than the %zu required", fn,
-                  workspace_bytes, need);
-  } else {
-    hipError_t e = hipMallocAsync(&scratch.ptr, need, s);
-    if (e != hipSuccess) return fail(PLX_ENOMEM, "%s: hipMallocAsync(%zu): %s", fn, need,
-                                     hipGetErrorString(e));
-    scratch.stream = s;
-    ws = scratch.ptr;
-  }
-  hipError_t e = plx::launch_stage_v(v, ws, B * H, L, d, s);
-  if (e != hipSuccess) return hip_fail("parallax_prefill stage_v launch", e);
-  e = plx::launch_prefill_bf16(q, k, ws, rho, gate, out, B, H, L, d, sc, s);
-  if (e != hipSuccess) return hip_fail("parallax_prefill launch", e);
-  return ok();
+  return prefill_impl("parallax_prefill", q, k, v, rho, gate, out, B, H, L, d, scale, dtype,
+                      workspace, workspace_bytes, (hipStream_t)stream, true);
 }
 
 int parallax_decode_default_split(int B, int H, int Lmax, int d) {
@@ -223,7 +283,7 @@ int parallax_decode_partials(const void* q, const void* kcache, const void* vcac
     return fail(PLX_EINVAL, "%s: null pointer", fn);
   hipError_t e = plx::launch_decode_split(q, kcache, vcache, rho, seqlens, partials, B, H, Lmax,
                                           d, split_keys, eff_scale(scale, d),
-                                          dtype == PLX_BF16, (hipStream_t)stream);
+                                          dtype == PLX_BF16, true, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail("parallax_decode_partials launch", e);
   return ok();
 }
@@ -237,7 +297,7 @@ int parallax_decode_combine(const float* partials, const float* gate, const int3
   if (!split_ok(split_keys, fn, &st)) return st;
   if (!partials || !gate || !seqlens || !out) return fail(PLX_EINVAL, "%s: null pointer", fn);
   hipError_t e = plx::launch_decode_combine(partials, gate, seqlens, out, B, H, Lmax, d,
-                                            split_keys, (hipStream_t)stream);
+                                            split_keys, true, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail("parallax_decode_combine launch", e);
   return ok();
 }
@@ -246,38 +306,31 @@ int parallax_decode(const void* q, const void* kcache, const void* vcache, const
                     const float* gate, float* out, const int32_t* seqlens, int B, int H,
                     int Lmax, int d, float scale, int dtype, int split_keys, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  const char* fn = "parallax_decode";
-  int st = PLX_OK;
-  if (!dims_ok(B, H, Lmax, d, fn, "Lmax", &st)) return st;
-  if (!streams_ok(B, H, fn, &st)) return st;
-  if (!dtype_ok(dtype, fn, &st)) return st;
-  const int C = split_keys > 0 ? split_keys : default_split(B, H, Lmax);
-  if (split_keys < 0 || !split_ok(C, fn, &st))
-    return split_keys < 0 ? fail(PLX_EINVAL, "%s: split_keys must be >= 0", fn) : st;
-  if (!q || !kcache || !vcache || !rho || !gate || !out || !seqlens)
-    return fail(PLX_EINVAL, "%s: null pointer", fn);
-  hipStream_t s = (hipStream_t)stream;
-  const size_t need = part_bytes(B, H, Lmax, d, C);
-  Scratch scratch;
-  void* ws = workspace;
-  if (ws) {
-    if (workspace_bytes < need)
-      return fail(PLX_EINVAL, "%s: workspace of %zu bytes is smaller than the %zu required", fn,
-                  workspace_bytes, need);
-  } else {
-    hipError_t e = hipMallocAsync(&scratch.ptr, need, s);
-    if (e != hipSuccess) return fail(PLX_ENOMEM, "%s: hipMallocAsync(%zu): %s", fn, need,
-                                     hipGetErrorString(e));
-    scratch.stream = s;
-    ws = scratch.ptr;
-  }
-  float* part = static_cast<float*>(ws);
-  hipError_t e = plx::launch_decode_split(q, kcache, vcache, rho, seqlens, part, B, H, Lmax, d,
-                                          C, eff_scale(scale, d), dtype == PLX_BF16, s);
-  if (e != hipSuccess) return hip_fail("parallax_decode split launch", e);
-  e = plx::launch_decode_combine(part, gate, seqlens, out, B, H, Lmax, d, C, s);
-  if (e != hipSuccess) return hip_fail("parallax_decode combine launch", e);
-  return ok();
+  return decode_impl("parallax_decode", q, kcache, vcache, rho, gate, out, seqlens, B, H, Lmax,
+                     d, scale, dtype, split_keys, workspace, workspace_bytes,
+                     (hipStream_t)stream, true);
+}
+
+int parallax_softmax_prefill(const void* q, const void* k, const void* v, float* out, int B,
+                             int H, int L, int d, float scale, int dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return prefill_impl("parallax_softmax_prefill", q, k, v, nullptr, nullptr, out, B, H, L, d,
+                      scale, dtype, workspace, workspace_bytes, (hipStream_t)stream, false);
+}
+
+int parallax_softmax_prefill_attend(const void* q, const void* k, const void* vt16, float* out,
+                                    int B, int H, int L, int d, float scale, void* stream) {
+  return attend_impl("parallax_softmax_prefill_attend", q, k, vt16, nullptr, nullptr, out, B,
+                     H, L, d, scale, (hipStream_t)stream, false);
+}
+
+int parallax_softmax_decode(const void* q, const void* kcache, const void* vcache, float* out,
+                            const int32_t* seqlens, int B, int H, int Lmax, int d, float scale,
+                            int dtype, int split_keys, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return decode_impl("parallax_softmax_decode", q, kcache, vcache, nullptr, nullptr, out,
+                     seqlens, B, H, Lmax, d, scale, dtype, split_keys, workspace,
+                     workspace_bytes, (hipStream_t)stream, false);
 }
 
 }  // extern "C"

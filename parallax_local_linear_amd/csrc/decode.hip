@@ -18,6 +18,10 @@
 //   groups of all four waves merge through LDS into one partial record.
 // decode_combine_kernel: one workgroup per (b,h) merges the records of its
 //   splits, rescaling by 2^(m_s - M), and applies the output formula.
+//
+// CORR = false compiles the covariance branch out of both kernels (no rho
+// reads, no <rho,k>, c or sum p r v; records of d+4 floats): plain softmax
+// decode over the same stream, the baseline for the cost of the correction.
 
 #include "plx_common.h"
 
@@ -33,9 +37,13 @@ struct DecCfg {
   static constexpr int NG = 4 * KPW;                 // lane groups per workgroup
 };
 
+// floats per split record: m, l, c, pad, sum p v [D] and, with the correction, sum p r v [D]
+template <int D, bool CORR>
+constexpr int rec_floats() { return (CORR ? 2 * D : D) + 4; }
+
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
 
-template <typename T, int D>
+template <typename T, int D, bool CORR>
 __global__ __launch_bounds__(256)
 void decode_split_kernel(const T* __restrict__ q, const T* __restrict__ kc,
                          const T* __restrict__ vc, const T* __restrict__ rho,
@@ -44,7 +52,8 @@ void decode_split_kernel(const T* __restrict__ q, const T* __restrict__ kc,
   using CF = DecCfg<T, D>;
   constexpr int EPL = CF::EPL, LPR = CF::LPR, KPW = CF::KPW, U = CF::U, NG = CF::NG;
   __shared__ float s_m[NG], s_l[NG], s_c[NG];
-  __shared__ float s_a[NG][D], s_b[NG][D];
+  constexpr int RF = rec_floats<D, CORR>();
+  __shared__ float s_a[NG][D], s_b[CORR ? NG : 1][D];
 
   const int s = blockIdx.x;
   const int bh = blockIdx.y;
@@ -63,7 +72,8 @@ void decode_split_kernel(const T* __restrict__ q, const T* __restrict__ kc,
 
   // this lane's slice of q and rho: features sub*EPL .. +EPL-1
   const u32x4 qw = *reinterpret_cast<const u32x4*>(q + (size_t)bh * D + sub * EPL);
-  const u32x4 rw = *reinterpret_cast<const u32x4*>(rho + (size_t)bh * D + sub * EPL);
+  u32x4 rw = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (CORR) rw = *reinterpret_cast<const u32x4*>(rho + (size_t)bh * D + sub * EPL);
 
   float A[EPL], Bv[EPL];
 #pragma unroll
@@ -96,18 +106,19 @@ void decode_split_kernel(const T* __restrict__ q, const T* __restrict__ kc,
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           sp = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw[w]), as_bf16x2(kr[u][w]), sp, false);
-          rp = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(rw[w]), as_bf16x2(kr[u][w]), rp, false);
+          if constexpr (CORR)
+            rp = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(rw[w]), as_bf16x2(kr[u][w]), rp, false);
         }
       } else {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const float kx = __uint_as_float(kr[u][w]);
           sp = fmaf(__uint_as_float(qw[w]), kx, sp);
-          rp = fmaf(__uint_as_float(rw[w]), kx, rp);
+          if constexpr (CORR) rp = fmaf(__uint_as_float(rw[w]), kx, rp);
         }
       }
       sp = group_sum<LPR>(sp);
-      rp = group_sum<LPR>(rp);
+      if constexpr (CORR) rp = group_sum<LPR>(rp);
       const int key = c0 + u * KPW + grp;
       sv[u] = (key < k_end) ? sp : -INFINITY;
       rv[u] = rp;
@@ -117,15 +128,18 @@ void decode_split_kernel(const T* __restrict__ q, const T* __restrict__ kc,
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     l_run *= alpha;
-    c_run *= alpha;
+    if constexpr (CORR) c_run *= alpha;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) { A[e] *= alpha; Bv[e] *= alpha; }
+    for (int e = 0; e < EPL; ++e) {
+      A[e] *= alpha;
+      if constexpr (CORR) Bv[e] *= alpha;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float p = __builtin_amdgcn_exp2f(fmaf(sv[u], sl2, -m_new));
       const float t = p * rv[u];
       l_run += p;
-      c_run += t;
+      if constexpr (CORR) c_run += t;
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -133,15 +147,17 @@ void decode_split_kernel(const T* __restrict__ q, const T* __restrict__ kc,
           const float v1 = bf16hi_to_f32(vr[u][w]);
           A[2 * w] = fmaf(p, v0, A[2 * w]);
           A[2 * w + 1] = fmaf(p, v1, A[2 * w + 1]);
-          Bv[2 * w] = fmaf(t, v0, Bv[2 * w]);
-          Bv[2 * w + 1] = fmaf(t, v1, Bv[2 * w + 1]);
+          if constexpr (CORR) {
+            Bv[2 * w] = fmaf(t, v0, Bv[2 * w]);
+            Bv[2 * w + 1] = fmaf(t, v1, Bv[2 * w + 1]);
+          }
         }
       } else {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const float vx = __uint_as_float(vr[u][w]);
           A[w] = fmaf(p, vx, A[w]);
-          Bv[w] = fmaf(t, vx, Bv[w]);
+          if constexpr (CORR) Bv[w] = fmaf(t, vx, Bv[w]);
         }
       }
     }
@@ -157,20 +173,20 @@ void decode_split_kernel(const T* __restrict__ q, const T* __restrict__ kc,
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     s_a[gi][sub * EPL + e] = A[e];
-    s_b[gi][sub * EPL + e] = Bv[e];
+    if constexpr (CORR) s_b[gi][sub * EPL + e] = Bv[e];
   }
   __syncthreads();
   float M = kMinit;
 #pragma unroll
   for (int i = 0; i < NG; ++i) M = fmaxf(M, s_m[i]);
-  float* rec = part + ((size_t)bh * S + s) * (2 * D + 4);
-  for (int t = tid; t < 2 * D; t += 256) {
+  float* rec = part + ((size_t)bh * S + s) * RF;
+  for (int t = tid; t < RF - 4; t += 256) {
     const int f = t % D;
     float acc = 0.f;
     if (t < D) {
 #pragma unroll
       for (int i = 0; i < NG; ++i) acc += __builtin_amdgcn_exp2f(s_m[i] - M) * s_a[i][f];
-    } else {
+    } else if constexpr (CORR) {
 #pragma unroll
       for (int i = 0; i < NG; ++i) acc += __builtin_amdgcn_exp2f(s_m[i] - M) * s_b[i][f];
     }
@@ -191,8 +207,9 @@ void decode_split_kernel(const T* __restrict__ q, const T* __restrict__ kc,
   }
 }
 
-// Merge the split records of one (b,h) and write o = o_sa - g (u - o_sa rbar).
-template <int D>
+// Merge the split records of one (b,h) and write o = o_sa - g (u - o_sa rbar)
+// (o = o_sa without the correction).
+template <int D, bool CORR>
 __global__ __launch_bounds__(D)
 void decode_combine_kernel(const float* __restrict__ part, const float* __restrict__ gate,
                            const int* __restrict__ seqlens, float* __restrict__ out,
@@ -207,57 +224,82 @@ void decode_combine_kernel(const float* __restrict__ part, const float* __restri
     o[f] = 0.f;
     return;
   }
-  const float* rec = part + (size_t)bh * S * (2 * D + 4);
+  constexpr int RF = rec_floats<D, CORR>();
+  const float* rec = part + (size_t)bh * S * RF;
   float M = kMinit;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, rec[(size_t)s * (2 * D + 4)]);
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, rec[(size_t)s * RF]);
   float l = 0.f, c = 0.f, a = 0.f, bv = 0.f;
   for (int s = 0; s < ns; ++s) {
-    const float* r = rec + (size_t)s * (2 * D + 4);
+    const float* r = rec + (size_t)s * RF;
     const float w = __builtin_amdgcn_exp2f(r[0] - M);
     l += w * r[1];
-    c += w * r[2];
     a += w * r[4 + f];
-    bv += w * r[4 + D + f];
+    if constexpr (CORR) {
+      c += w * r[2];
+      bv += w * r[4 + D + f];
+    }
   }
   const float inv = 1.0f / l;
   const float osa = a * inv;
-  const float uu = bv * inv;
-  o[f] = osa - gate[h] * (uu - osa * (c * inv));
+  if constexpr (CORR) {
+    const float uu = bv * inv;
+    o[f] = osa - gate[h] * (uu - osa * (c * inv));
+  } else {
+    o[f] = osa;
+  }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool CORR>
 static hipError_t launch_split_t(const void* q, const void* kc, const void* vc,
                                  const void* rho, const int* seqlens, float* part, int B,
                                  int H, int Lmax, int C, float sl2, hipStream_t s) {
   const int S = (Lmax + C - 1) / C;
-  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3((unsigned)S, (unsigned)(B * H)),
+  hipLaunchKernelGGL((decode_split_kernel<T, D, CORR>), dim3((unsigned)S, (unsigned)(B * H)),
                      dim3(256), 0, s, (const T*)q, (const T*)kc, (const T*)vc,
                      (const T*)rho, seqlens, part, H, Lmax, C, S, sl2);
   return hipGetLastError();
 }
 
+template <bool CORR>
+static hipError_t launch_split_c(const void* q, const void* kc, const void* vc, const void* rho,
+                                 const int* seqlens, float* part, int B, int H, int Lmax, int d,
+                                 int C, float sl2, bool bf16, hipStream_t s) {
+  if (bf16) {
+    if (d == 128)
+      return launch_split_t<__bf16, 128, CORR>(q, kc, vc, rho, seqlens, part, B, H, Lmax, C, sl2, s);
+    return launch_split_t<__bf16, 64, CORR>(q, kc, vc, rho, seqlens, part, B, H, Lmax, C, sl2, s);
+  }
+  if (d == 128)
+    return launch_split_t<float, 128, CORR>(q, kc, vc, rho, seqlens, part, B, H, Lmax, C, sl2, s);
+  return launch_split_t<float, 64, CORR>(q, kc, vc, rho, seqlens, part, B, H, Lmax, C, sl2, s);
+}
+
 hipError_t launch_decode_split(const void* q, const void* kc, const void* vc, const void* rho,
                                const int* seqlens, float* part, int B, int H, int Lmax, int d,
-                               int C, float scale, bool bf16, hipStream_t s) {
+                               int C, float scale, bool bf16, bool corr, hipStream_t s) {
   const float sl2 = scale * kLog2e;
-  if (bf16) {
-    if (d == 128) return launch_split_t<__bf16, 128>(q, kc, vc, rho, seqlens, part, B, H, Lmax, C, sl2, s);
-    return launch_split_t<__bf16, 64>(q, kc, vc, rho, seqlens, part, B, H, Lmax, C, sl2, s);
-  }
-  if (d == 128) return launch_split_t<float, 128>(q, kc, vc, rho, seqlens, part, B, H, Lmax, C, sl2, s);
-  return launch_split_t<float, 64>(q, kc, vc, rho, seqlens, part, B, H, Lmax, C, sl2, s);
+  if (corr) return launch_split_c<true>(q, kc, vc, rho, seqlens, part, B, H, Lmax, d, C, sl2, bf16, s);
+  return launch_split_c<false>(q, kc, vc, rho, seqlens, part, B, H, Lmax, d, C, sl2, bf16, s);
+}
+
+template <int D, bool CORR>
+static void launch_combine_t(const float* part, const float* gate, const int* seqlens,
+                             float* out, int B, int H, int Lmax, int C, int S, hipStream_t s) {
+  hipLaunchKernelGGL((decode_combine_kernel<D, CORR>), dim3((unsigned)(B * H)), dim3(D), 0, s,
+                     part, gate, seqlens, out, H, Lmax, C, S);
 }
 
 hipError_t launch_decode_combine(const float* part, const float* gate, const int* seqlens,
-                                 float* out, int B, int H, int Lmax, int d, int C,
+                                 float* out, int B, int H, int Lmax, int d, int C, bool corr,
                                  hipStream_t s) {
   const int S = (Lmax + C - 1) / C;
-  if (d == 128)
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((unsigned)(B * H)), dim3(128), 0, s,
-                       part, gate, seqlens, out, H, Lmax, C, S);
-  else
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((unsigned)(B * H)), dim3(64), 0, s,
-                       part, gate, seqlens, out, H, Lmax, C, S);
+  if (d == 128) {
+    if (corr) launch_combine_t<128, true>(part, gate, seqlens, out, B, H, Lmax, C, S, s);
+    else launch_combine_t<128, false>(part, gate, seqlens, out, B, H, Lmax, C, S, s);
+  } else {
+    if (corr) launch_combine_t<64, true>(part, gate, seqlens, out, B, H, Lmax, C, S, s);
+    else launch_combine_t<64, false>(part, gate, seqlens, out, B, H, Lmax, C, S, s);
+  }
   return hipGetLastError();
 }
 

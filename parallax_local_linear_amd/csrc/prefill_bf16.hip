@@ -67,6 +67,28 @@ constexpr int PF_BC = 64;       // keys per tile
 #ifndef PLX_PF_MINW_D64
 #define PLX_PF_MINW_D64 4
 #endif
+// The same three choices for the softmax-only variant (correction compiled out),
+// tuned on their own: without R, T and their accumulators the d=128 kernel
+// needs 104 VGPRs un-pipelined, so two 8-wave workgroups share a CU (four waves
+// per SIMD), which beats the pipelined 4-wave shape by about 20%.
+#ifndef PLX_SM_NW_D128
+#define PLX_SM_NW_D128 8
+#endif
+#ifndef PLX_SM_NW_D64
+#define PLX_SM_NW_D64 PLX_PF_NW_D64
+#endif
+#ifndef PLX_SM_PIPE_D128
+#define PLX_SM_PIPE_D128 0
+#endif
+#ifndef PLX_SM_PIPE_D64
+#define PLX_SM_PIPE_D64 PLX_PF_PIPE_D64
+#endif
+#ifndef PLX_SM_MINW_D128
+#define PLX_SM_MINW_D128 PLX_PF_MINW_D128
+#endif
+#ifndef PLX_SM_MINW_D64
+#define PLX_SM_MINW_D64 PLX_PF_MINW_D64
+#endif
 // Rescale slack in log2 units: P = 2^(s - m) may grow to 2^kRescaleSlack before
 // the running max m is moved.  Keeps fp16 P <= 16 and T = P*R within fp16 range
 // for |<rho,k>| < 4094.
@@ -101,8 +123,12 @@ __host__ __device__ constexpr int vt_key_of_pos(int p) {
 
 // Second launch bound: at least two waves per SIMD, which caps the register
 // budget at 256 per lane and keeps every MFMA operand in VGPRs.
-template <int D, int NW, bool PIPE>
-__global__ __launch_bounds__(64 * NW, (D == 64 ? PLX_PF_MINW_D64 : PLX_PF_MINW_D128))
+// CORR = false compiles the covariance branch out (no R, T, A_r or c): plain
+// causal softmax attention through the same staging, tiling and schedule, the
+// baseline for the cost of the correction.
+template <int D, int NW, bool PIPE, bool CORR>
+__global__ __launch_bounds__(64 * NW, CORR ? (D == 64 ? PLX_PF_MINW_D64 : PLX_PF_MINW_D128)
+                                          : (D == 64 ? PLX_SM_MINW_D64 : PLX_SM_MINW_D128))
 void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                          const _Float16* __restrict__ vt, const __bf16* __restrict__ rho,
                          const float* __restrict__ gate, float* __restrict__ out,
@@ -134,11 +160,13 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   bf16x8 qf[KSTEPS], rf[KSTEPS];
   if (qi < L) {
     const bf16x8* qp = reinterpret_cast<const bf16x8*>(q + head + (size_t)qi * D);
-    const bf16x8* rp = reinterpret_cast<const bf16x8*>(rho + head + (size_t)qi * D);
+    const bf16x8* rp = CORR ? reinterpret_cast<const bf16x8*>(rho + head + (size_t)qi * D)
+                            : nullptr;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       qf[kk] = qp[4 * kk + g4];
-      rf[kk] = rp[4 * kk + g4];
+      if constexpr (CORR) rf[kk] = rp[4 * kk + g4];
+      else rf[kk] = bf16x8{};
     }
   } else {
 #pragma unroll
@@ -224,11 +252,13 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       for (int kk = 0; kk < KSTEPS; ++kk)
         a[kk] = *reinterpret_cast<const bf16x8*>(ks + LY::k_off(16 * kb + c16, 4 * kk + g4));
       sa[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], qf[0], f32x4{}, 0, 0, 0);
-      ra[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], rf[0], f32x4{}, 0, 0, 0);
+      if constexpr (CORR)
+        ra[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], rf[0], f32x4{}, 0, 0, 0);
 #pragma unroll
       for (int kk = 1; kk < KSTEPS; ++kk) {
         sa[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], qf[kk], sa[kb], 0, 0, 0);
-        ra[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], rf[kk], ra[kb], 0, 0, 0);
+        if constexpr (CORR)
+          ra[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], rf[kk], ra[kb], 0, 0, 0);
       }
     }
   };
@@ -283,11 +313,11 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       acc_l *= alpha;
-      acc_c *= alpha;
+      if constexpr (CORR) acc_c *= alpha;
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
         acc_o[fb] *= alpha;
-        acc_r[fb] *= alpha;
+        if constexpr (CORR) acc_r[fb] *= alpha;
       }
     }
   };
@@ -304,19 +334,21 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float p = __builtin_amdgcn_exp2f(fmaf(sa[2 * t + hh][j], sl2, -m_use));
-          const float tv = p * ra[2 * t + hh][j];
+          const float tv = CORR ? p * ra[2 * t + hh][j] : 0.f;
           pf[4 * hh + j] = (_Float16)p;
-          tf[4 * hh + j] = (_Float16)tv;
+          if constexpr (CORR) tf[4 * hh + j] = (_Float16)tv;
         }
       }
       acc_l = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8, pf, acc_l, 0, 0, 0);
-      acc_c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8, tf, acc_c, 0, 0, 0);
+      if constexpr (CORR)
+        acc_c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8, tf, acc_c, 0, 0, 0);
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
         const f16x8 va =
             *reinterpret_cast<const f16x8*>(vs + LY::v_off(16 * fb + c16, 4 * t + g4));
         acc_o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pf, acc_o[fb], 0, 0, 0);
-        acc_r[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, tf, acc_r[fb], 0, 0, 0);
+        if constexpr (CORR)
+          acc_r[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, tf, acc_r[fb], 0, 0, 0);
       }
     }
   };
@@ -396,7 +428,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   if (qi < L) {
     const float inv = 1.0f / l_tot;
     const float rbar = c_tot * inv;
-    const float gh = gate[h];
+    const float gh = CORR ? gate[h] : 0.f;
     float* orow = out + head + (size_t)qi * D;
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb) {
@@ -404,8 +436,12 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float osa = acc_o[fb][j] * inv;
-        const float uu = acc_r[fb][j] * inv;
-        o[j] = osa - gh * (uu - osa * rbar);
+        if constexpr (CORR) {
+          const float uu = acc_r[fb][j] * inv;
+          o[j] = osa - gh * (uu - osa * rbar);
+        } else {
+          o[j] = osa;
+        }
       }
       *reinterpret_cast<f32x4*>(orow + 16 * fb + 4 * g4) = o;
     }
@@ -460,27 +496,37 @@ hipError_t launch_stage_v(const void* v, void* vt, int BH, int L, int d, hipStre
   return hipGetLastError();
 }
 
-template <int D, int NW, bool PIPE>
+template <int D, int NW, bool PIPE, bool CORR>
 static hipError_t launch_prefill_t(const void* q, const void* k, const void* vt,
                                    const void* rho, const float* gate, float* out, int B,
                                    int H, int L, float sl2, hipStream_t s) {
   const int BH = B * H;
   const int n_qt = (L + 16 * NW - 1) / (16 * NW);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, PIPE>), dim3((unsigned)(BH * n_qt)), dim3(64 * NW),
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, PIPE, CORR>), dim3((unsigned)(BH * n_qt)), dim3(64 * NW),
                      0, s, (const __bf16*)q, (const __bf16*)k, (const _Float16*)vt,
                      (const __bf16*)rho, gate, out, H, L, BH, n_qt, sl2);
   return hipGetLastError();
 }
 
+template <bool CORR>
+static hipError_t launch_prefill_c(const void* q, const void* k, const void* vt, const void* rho,
+                                   const float* gate, float* out, int B, int H, int L, int d,
+                                   float sl2, hipStream_t s) {
+  constexpr int nw128 = CORR ? PLX_PF_NW_D128 : PLX_SM_NW_D128;
+  constexpr int nw64 = CORR ? PLX_PF_NW_D64 : PLX_SM_NW_D64;
+  constexpr bool pipe128 = CORR ? (PLX_PF_PIPE_D128 != 0) : (PLX_SM_PIPE_D128 != 0);
+  constexpr bool pipe64 = CORR ? (PLX_PF_PIPE_D64 != 0) : (PLX_SM_PIPE_D64 != 0);
+  if (d == 128)
+    return launch_prefill_t<128, nw128, pipe128, CORR>(q, k, vt, rho, gate, out, B, H, L, sl2, s);
+  return launch_prefill_t<64, nw64, pipe64, CORR>(q, k, vt, rho, gate, out, B, H, L, sl2, s);
+}
+
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* vt, const void* rho,
                                const float* gate, float* out, int B, int H, int L, int d,
-                               float scale, hipStream_t s) {
+                               float scale, bool corr, hipStream_t s) {
   const float sl2 = scale * kLog2e;
-  if (d == 128)
-    return launch_prefill_t<128, PLX_PF_NW_D128, (PLX_PF_PIPE_D128 != 0)>(q, k, vt, rho, gate,
-                                                                          out, B, H, L, sl2, s);
-  return launch_prefill_t<64, PLX_PF_NW_D64, (PLX_PF_PIPE_D64 != 0)>(q, k, vt, rho, gate, out,
-                                                                      B, H, L, sl2, s);
+  if (corr) return launch_prefill_c<true>(q, k, vt, rho, gate, out, B, H, L, d, sl2, s);
+  return launch_prefill_c<false>(q, k, vt, rho, gate, out, B, H, L, d, sl2, s);
 }
 
 }  // namespace plx

@@ -9,7 +9,8 @@
 // 16*j + 4*part).  Keys stream through LDS in tiles of 32; per tile the 4 lanes
 // form the partial dot products <q,k_j> and <rho,k_j>, reduce them with DPP,
 // update the online-softmax state once per tile, and accumulate sum p v and
-// sum p r v for their features.
+// sum p r v for their features.  CORR = false compiles the covariance branch
+// out: plain causal softmax attention on the same schedule.
 
 #include "plx_common.h"
 
@@ -18,7 +19,7 @@ namespace plx {
 constexpr int PF32_QB = 64;
 constexpr int PF32_KB = 32;
 
-template <int D>
+template <int D, bool CORR>
 __global__ __launch_bounds__(256)
 void prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                         const float* __restrict__ v, const float* __restrict__ rho,
@@ -42,7 +43,8 @@ void prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k
   for (int j = 0; j < NJ; ++j) {
     if (qi < L) {
       qr[j] = *reinterpret_cast<const f32x4*>(q + head + (size_t)qi * D + 16 * j + 4 * part);
-      rr[j] = *reinterpret_cast<const f32x4*>(rho + head + (size_t)qi * D + 16 * j + 4 * part);
+      rr[j] = CORR ? *reinterpret_cast<const f32x4*>(rho + head + (size_t)qi * D + 16 * j + 4 * part)
+                   : f32x4{};
     } else {
       qr[j] = f32x4{};
       rr[j] = f32x4{};
@@ -80,11 +82,11 @@ void prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           sp = fmaf(qr[jj][e], kv[e], sp);
-          rp = fmaf(rr[jj][e], kv[e], rp);
+          if constexpr (CORR) rp = fmaf(rr[jj][e], kv[e], rp);
         }
       }
       sp = group_sum<4>(sp);
-      rp = group_sum<4>(rp);
+      if constexpr (CORR) rp = group_sum<4>(rp);
       s[j] = (k0 + j <= qi) ? sp : -INFINITY;
       r[j] = rp;
       mx = fmaxf(mx, s[j]);
@@ -93,25 +95,25 @@ void prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k
     const float alpha = exp2f(m_run - m_new);
     m_run = m_new;
     l_run *= alpha;
-    c_run *= alpha;
+    if constexpr (CORR) c_run *= alpha;
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
       A[jj] *= alpha;
-      Bv[jj] *= alpha;
+      if constexpr (CORR) Bv[jj] *= alpha;
     }
 #pragma unroll
     for (int j = 0; j < PF32_KB; ++j) {
       const float p = exp2f(fmaf(s[j], sl2, -m_new));
       const float t = p * r[j];
       l_run += p;
-      c_run += t;
+      if constexpr (CORR) c_run += t;
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) {
         const f32x4 vv = *reinterpret_cast<const f32x4*>(vs + j * D + 16 * jj + 4 * part);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           A[jj][e] = fmaf(p, vv[e], A[jj][e]);
-          Bv[jj][e] = fmaf(t, vv[e], Bv[jj][e]);
+          if constexpr (CORR) Bv[jj][e] = fmaf(t, vv[e], Bv[jj][e]);
         }
       }
     }
@@ -120,36 +122,47 @@ void prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k
   if (qi < L) {
     const float inv = 1.0f / l_run;
     const float rbar = c_run * inv;
-    const float gh = gate[h];
+    const float gh = CORR ? gate[h] : 0.f;
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
       f32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float osa = A[jj][e] * inv;
-        const float uu = Bv[jj][e] * inv;
-        o[e] = osa - gh * (uu - osa * rbar);
+        if constexpr (CORR) {
+          const float uu = Bv[jj][e] * inv;
+          o[e] = osa - gh * (uu - osa * rbar);
+        } else {
+          o[e] = osa;
+        }
       }
       *reinterpret_cast<f32x4*>(out + head + (size_t)qi * D + 16 * jj + 4 * part) = o;
     }
   }
 }
 
+template <int D, bool CORR>
+static void launch_f32_t(const void* q, const void* k, const void* v, const void* rho,
+                         const float* gate, float* out, int H, int L, int BH, int n_qt,
+                         float sl2, hipStream_t s) {
+  hipLaunchKernelGGL((prefill_f32_kernel<D, CORR>), dim3((unsigned)(BH * n_qt)), dim3(256), 0,
+                     s, (const float*)q, (const float*)k, (const float*)v, (const float*)rho,
+                     gate, out, H, L, BH, n_qt, sl2);
+}
+
 hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, const void* rho,
                               const float* gate, float* out, int B, int H, int L, int d,
-                              float scale, hipStream_t s) {
+                              float scale, bool corr, hipStream_t s) {
   const int BH = B * H;
   const int n_qt = (L + PF32_QB - 1) / PF32_QB;
-  const dim3 grid((unsigned)(BH * n_qt));
   const float sl2 = scale * kLog2e;
-  if (d == 128)
-    hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, dim3(256), 0, s, (const float*)q,
-                       (const float*)k, (const float*)v, (const float*)rho, gate, out, H, L,
-                       BH, n_qt, sl2);
-  else
-    hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, dim3(256), 0, s, (const float*)q,
-                       (const float*)k, (const float*)v, (const float*)rho, gate, out, H, L,
-                       BH, n_qt, sl2);
+  if (d == 128) {
+    if (corr) launch_f32_t<128, true>(q, k, v, rho, gate, out, H, L, BH, n_qt, sl2, s);
+    else launch_f32_t<128, false>(q, k, v, rho, gate, out, H, L, BH, n_qt, sl2, s);
+  } else {
+    if (corr) launch_f32_t<64, true>(q, k, v, rho, gate, out, H, L, BH, n_qt, sl2, s);
+    else launch_f32_t<64, false>(q, k, v, rho, gate, out, H, L, BH, n_qt, sl2, s);
+  }
   return hipGetLastError();
 }
 

@@ -126,6 +126,39 @@ void decode_rejections() {
          "parallax_decode_combine", "combine split 96");
 }
 
+// The softmax-only entry points share the Parallax calls' validation; they take
+// no rho or gate.
+void softmax_rejections() {
+  const char* fp = "parallax_softmax_prefill";
+  expect(parallax_softmax_prefill(P(0), P(1), P(2), F(3), 1, 0, 64, 64, 0.f, PLX_BF16, nullptr, 0,
+                                  nullptr), PLX_EINVAL, fp, "softmax prefill H=0");
+  expect(parallax_softmax_prefill(P(0), P(1), nullptr, F(3), 1, 1, 64, 64, 0.f, PLX_F32, nullptr,
+                                  0, nullptr), PLX_EINVAL, fp, "softmax prefill null v");
+  expect(parallax_softmax_prefill(P(0), P(1), P(2), F(3), 1, 1, 64, 256, 0.f, PLX_BF16, nullptr,
+                                  0, nullptr), PLX_EUNSUPPORTED, fp, "softmax prefill d=256");
+  expect(parallax_softmax_prefill(P(0), P(1), P(2), F(3), 1, 1, 64, 64, 0.f, 5, nullptr, 0,
+                                  nullptr), PLX_EUNSUPPORTED, fp, "softmax prefill dtype 5");
+  const size_t need = parallax_prefill_workspace_bytes(1, 2, 300, 64, PLX_BF16);
+  expect(parallax_softmax_prefill(P(0), P(1), P(2), F(3), 1, 2, 300, 64, 0.f, PLX_BF16, P(4),
+                                  need - 1, nullptr), PLX_EINVAL, fp,
+         "softmax prefill workspace too small");
+  expect(parallax_softmax_prefill_attend(P(0), P(1), nullptr, F(3), 1, 1, 64, 64, 0.f, nullptr),
+         PLX_EINVAL, "parallax_softmax_prefill_attend", "softmax attend null vt16");
+  expect(parallax_softmax_prefill_attend(P(0), P(1), P(2), F(3), 1, 1, -5, 64, 0.f, nullptr),
+         PLX_EINVAL, "parallax_softmax_prefill_attend", "softmax attend L<0");
+  const char* fd = "parallax_softmax_decode";
+  expect(parallax_softmax_decode(P(0), P(1), P(2), F(3), nullptr, 1, 1, 64, 128, 0.f, PLX_BF16, 0,
+                                 nullptr, 0, nullptr), PLX_EINVAL, fd, "softmax decode null seqlens");
+  expect(parallax_softmax_decode(P(0), P(1), P(2), F(3), I(4), 1, 1, 64, 128, 0.f, PLX_BF16, 96,
+                                 nullptr, 0, nullptr), PLX_EINVAL, fd, "softmax decode split 96");
+  expect(parallax_softmax_decode(P(0), P(1), P(2), F(3), I(4), 65536, 1, 64, 128, 0.f, PLX_BF16, 0,
+                                 nullptr, 0, nullptr), PLX_EINVAL, fd, "softmax decode B*H > 65535");
+  const size_t dneed = parallax_decode_workspace_bytes(2, 2, 900, 128, 256);
+  expect(parallax_softmax_decode(P(0), P(1), P(2), F(3), I(4), 2, 2, 900, 128, 0.f, PLX_F32, 256,
+                                 P(5), dneed - 4, nullptr), PLX_EINVAL, fd,
+         "softmax decode workspace too small");
+}
+
 // Without a device, valid arguments reach the HIP runtime: the launch and
 // allocation failures must be reported, not crash.
 void no_device_failures() {
@@ -154,6 +187,24 @@ void no_device_failures() {
          "partials launch failure");
   expect(parallax_decode_combine(F(0), F(1), I(2), F(3), 1, 1, 64, 64, 64, nullptr), PLX_EHIP,
          "parallax_decode_combine", "combine launch failure");
+  // the softmax-only calls: null rho and gate are fine, the launch still fails
+  expect(parallax_softmax_prefill(P(0), P(1), P(2), F(3), 1, 1, 64, 128, 0.f, PLX_BF16, P(6), ws * 2,
+                                  nullptr), PLX_EHIP, "parallax_softmax_prefill",
+         "softmax prefill launch failure");
+  expect(parallax_softmax_prefill(P(0), P(1), P(2), F(3), 1, 1, 64, 64, 0.f, PLX_BF16, nullptr, 0,
+                                  nullptr), PLX_ENOMEM, "parallax_softmax_prefill",
+         "softmax prefill allocation failure");
+  expect(parallax_softmax_prefill(P(0), P(1), P(2), F(3), 1, 1, 64, 64, 0.f, PLX_F32, nullptr, 0,
+                                  nullptr), PLX_EHIP, "parallax_softmax_prefill",
+         "softmax fp32 prefill launch failure");
+  expect(parallax_softmax_prefill_attend(P(0), P(1), P(2), F(3), 1, 1, 64, 64, 0.f, nullptr),
+         PLX_EHIP, "parallax_softmax_prefill_attend", "softmax attend launch failure");
+  expect(parallax_softmax_decode(P(0), P(1), P(2), F(3), I(4), 1, 1, 64, 128, 0.f, PLX_F32, 64,
+                                 P(7), dws, nullptr), PLX_EHIP, "parallax_softmax_decode",
+         "softmax decode launch failure");
+  expect(parallax_softmax_decode(P(0), P(1), P(2), F(3), I(4), 1, 1, 64, 128, 0.f, PLX_F32, 0,
+                                 nullptr, 0, nullptr), PLX_ENOMEM, "parallax_softmax_decode",
+         "softmax decode allocation failure");
 }
 
 void error_text_is_per_thread() {
@@ -173,6 +224,7 @@ int main() {
   workspace_sizes();
   prefill_rejections();
   decode_rejections();
+  softmax_rejections();
   error_text_is_per_thread();
   int n_dev = 0;
   if (hipGetDeviceCount(&n_dev) != hipSuccess) n_dev = 0;

@@ -95,6 +95,21 @@ def test_decode_rejects_bad_arguments(lib):
     assert h(x, x, x, NULL, 1, 1, 64, 128, 64, NULL) == PLX_EINVAL
 
 
+def test_softmax_calls_reject_bad_arguments(lib):
+    x = ctypes.c_void_p(0x1000)
+    f = lib.parallax_softmax_prefill
+    assert f(NULL, x, x, x, 1, 1, 64, 128, 0.0, 1, NULL, 0, NULL) == PLX_EINVAL
+    assert b"parallax_softmax_prefill" in lib.parallax_last_error()
+    assert f(x, x, x, x, 1, 1, 64, 48, 0.0, 1, NULL, 0, NULL) == PLX_EUNSUPPORTED
+    assert f(x, x, x, x, 1, 1, 64, 128, 0.0, 1, x, 100, NULL) == PLX_EINVAL
+    g = lib.parallax_softmax_prefill_attend
+    assert g(x, x, x, NULL, 1, 1, 64, 128, 0.0, NULL) == PLX_EINVAL
+    h = lib.parallax_softmax_decode
+    assert h(x, x, x, x, NULL, 1, 1, 64, 128, 0.0, 1, 0, NULL, 0, NULL) == PLX_EINVAL
+    assert h(x, x, x, x, x, 1, 1, 64, 128, 0.0, 9, 0, NULL, 0, NULL) == PLX_EUNSUPPORTED
+    assert h(x, x, x, x, x, 1, 1, 64, 128, 0.0, 1, 32, NULL, 0, NULL) == PLX_EINVAL
+
+
 def test_binding_raises_without_library(monkeypatch, tmp_path):
     """The product path has no fallback: a missing library is an error."""
     monkeypatch.setattr(_native, "_lib", None)
@@ -112,3 +127,7 @@ def test_binding_requires_gpu_tensors():
         plx.prefill(x, x, x, x, torch.ones(1))
     with pytest.raises(ValueError, match="GPU"):
         plx.decode(x[:, :, 0], x, x, x[:, :, 0], torch.ones(1), torch.ones(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU"):
+        plx.softmax_prefill(x, x, x)
+    with pytest.raises(ValueError, match="GPU"):
+        plx.softmax_decode(x[:, :, 0], x, x, torch.ones(1, dtype=torch.int32))

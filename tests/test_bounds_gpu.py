@@ -112,6 +112,48 @@ def test_decode_writes_stay_in_bounds(dtype, d):
     _unchanged(inp, snap)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_softmax_writes_stay_in_bounds(dtype, d):
+    """The softmax-only entry points: same guard bands; rho and gate are not
+    passed at all."""
+    lib = _native.lib()
+    code = _native.PLX_BF16 if dtype == "bf16" else _native.PLX_F32
+    stream = torch.cuda.current_stream().cuda_stream
+    B, H, L = 2, 3, 130
+    inp = wl.prefill_inputs(B, H, L, d, dtype, seed=630 + d, device="cuda")
+    snap = _snapshot(inp)
+    out_bytes = B * H * L * d * 4
+    out_buf, out_ptr = _guarded(out_bytes)
+    ws_bytes = lib.parallax_prefill_workspace_bytes(B, H, L, d, code)
+    ws_buf, ws_ptr = _guarded(ws_bytes) if ws_bytes else (None, None)
+    st = lib.parallax_softmax_prefill(inp["q"].data_ptr(), inp["k"].data_ptr(),
+                                      inp["v"].data_ptr(), out_ptr, B, H, L, d, 0.0, code,
+                                      ws_ptr, ws_bytes, stream)
+    assert st == 0, lib.parallax_last_error()
+    torch.cuda.synchronize()
+    _check_guards(out_buf, out_bytes, "softmax prefill out")
+    if ws_buf is not None:
+        _check_guards(ws_buf, ws_bytes, "softmax prefill workspace")
+    _unchanged(inp, snap)
+    B, H, Lmax, split = 3, 2, 700, 128
+    inp = wl.decode_inputs(B, H, Lmax, d, dtype, seed=640 + d, device="cuda",
+                           seqlens=[700, 129, 0])
+    snap = _snapshot(inp)
+    out_bytes = B * H * d * 4
+    out_buf, out_ptr = _guarded(out_bytes)
+    ws_bytes = lib.parallax_decode_workspace_bytes(B, H, Lmax, d, split)
+    ws_buf, ws_ptr = _guarded(ws_bytes)
+    st = lib.parallax_softmax_decode(inp["q"].data_ptr(), inp["kcache"].data_ptr(),
+                                     inp["vcache"].data_ptr(), out_ptr, inp["seqlens"].data_ptr(),
+                                     B, H, Lmax, d, 0.0, code, split, ws_ptr, ws_bytes, stream)
+    assert st == 0, lib.parallax_last_error()
+    torch.cuda.synchronize()
+    _check_guards(out_buf, out_bytes, "softmax decode out")
+    _check_guards(ws_buf, ws_bytes, "softmax decode workspace", fully_written=False)
+    _unchanged(inp, snap)
+
+
 def test_nan_in_a_query_row_stays_in_that_row():
     """A NaN in one query row turns that output row into NaN.  Rows outside its
     16-row block (one wave) are bit-identical to a clean run; rows inside it
