@@ -1,4 +1,5 @@
-"""CPU oracle of the Parallax attention forward pass (test infrastructure only).
+"""CPU oracle of the Parallax attention forward and backward pass (test
+infrastructure only).
 
 Only the test suite, the package smoke check and the benchmark's CPU-baseline
 leg may import this package; the product path never does.
@@ -11,6 +12,10 @@ from .parallax_oracle import (  # noqa: F401
     prefill,
     prefill_explicit,
     prefill_head,
+    prefill_backward,
+    prefill_head_backward,
+    prefill_head_train,
     prefill_rows,
+    prefill_train,
     softmax_weights,
 )

@@ -1,4 +1,4 @@
-"""CPU oracle for the Parallax attention forward pass.
+"""CPU oracle for the Parallax attention forward pass and its gradients.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the package's smoke check and
 the benchmark's CPU-baseline leg may import this module.  The product path (the
@@ -216,3 +216,124 @@ def decode_explicit(q, kcache, vcache, rho, gate, seqlens, scale=None, streams=N
         out[b, h] = explicit_row(qf[b, h], _f64(kcache[b, h, :n]), _f64(vcache[b, h, :n]),
                                  rf[b, h], gf[h], sc)[0]
     return out
+
+
+# ----------------------------------------------------------------- training
+# The pages describe no backward pass; pretraining (section "Results") implies
+# one.  What follows is the exact derivative of Eq. 2 (section "Core
+# mechanism") with respect to q, k, v, rho and the per-head gate, written out
+# by hand from the expanded form.  With S = scale Q K^T (causal), W its row
+# softmax, R = rho K^T, rbar = rowsum(W*R), O_sa = W V, U = (W*R) V and the
+# correction C = U - O_sa rbar (= Sigma^(i) rho_i row by row), the output is
+# O = O_sa - g C.  Given dO:
+#   Delta = dO V^T,  D = rowsum(dO * O_sa),  F = rowsum(dO * O)
+#   dV   = (W * (1 - g (R - rbar)))^T dO
+#   dR   = -g W * (Delta - D)
+#   dS   = W * (Delta * (1 - g (R - rbar)) + g (R - rbar) D - F)
+#   dQ   = scale dS K,  dK = scale dS^T Q + dR^T rho,  drho = dR K
+#   dg   = -sum over rows of rowsum(dO * C)
+# The forward statistics a backward pass needs besides O are the natural-log
+# partition function lse_i = log sum_j exp(s_ij), rbar_i and the correction C_i
+# (O alone does not determine O_sa when g != 0).  Pinned in the CPU tests
+# against torch autograd in fp64 and central differences.
+
+def _head_forward_blocks(q, k, v, rho, g, scale, r, n):
+    """Forward quantities of the rows r (all < n) of one head, keys 0..n-1."""
+    S = scale * (q[r] @ k[:n].T)
+    causal = np.arange(n)[None, :] <= r[:, None]
+    S = np.where(causal, S, -np.inf)
+    mx = S.max(axis=1, keepdims=True)
+    E = np.exp(S - mx)
+    Z = E.sum(axis=1, keepdims=True)
+    W = E / Z
+    lse = (mx + np.log(Z))[:, 0]
+    R = rho[r] @ k[:n].T
+    WR = W * R
+    o_sa = W @ v[:n]
+    u = WR @ v[:n]
+    rbar = WR.sum(axis=1, keepdims=True)
+    corr = u - o_sa * rbar
+    return W, R, rbar, o_sa, corr, lse
+
+
+def prefill_head_train(q, k, v, rho, g, scale, block=512):
+    """Forward pass of one head that also returns the statistics a backward pass
+    needs: (out [L,d_v], lse [L], rbar [L], corr [L,d_v])."""
+    L = q.shape[0]
+    out = np.empty((L, v.shape[1]))
+    corr = np.empty((L, v.shape[1]))
+    lse = np.empty(L)
+    rbar = np.empty(L)
+    for s0 in range(0, L, block):
+        r = np.arange(s0, min(s0 + block, L))
+        _, _, rb, o_sa, c, ls = _head_forward_blocks(q, k, v, rho, g, scale, r, int(r[-1]) + 1)
+        out[r] = o_sa - g * c
+        corr[r] = c
+        lse[r] = ls
+        rbar[r] = rb[:, 0]
+    return out, lse, rbar, corr
+
+
+def prefill_train(q, k, v, rho, gate, scale=None, heads=None):
+    """Causal prefill with its saved statistics, all heads (or the listed (b, h)
+    pairs; the rest stays NaN).  Returns dict(out, lse, rbar, corr)."""
+    q, k, v, rho, gate = map(_f64, (q, k, v, rho, gate))
+    B, H, L, dk = q.shape
+    sc = _default_scale(dk, scale)
+    res = dict(out=np.full(v.shape, np.nan), lse=np.full((B, H, L), np.nan),
+               rbar=np.full((B, H, L), np.nan), corr=np.full(v.shape, np.nan))
+    todo = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b, h in todo:
+        o, ls, rb, c = prefill_head_train(q[b, h], k[b, h], v[b, h], rho[b, h], gate[h], sc)
+        res["out"][b, h], res["lse"][b, h], res["rbar"][b, h], res["corr"][b, h] = o, ls, rb, c
+    return res
+
+
+def prefill_head_backward(q, k, v, rho, g, scale, dout, block=512):
+    """Gradients of one causal head: returns (dq, dk, dv, drho, dg) where dg is
+    this head's contribution to the gate gradient.  Rows are processed a block
+    at a time; the key-side gradients (dk, dv) are sums over all row blocks."""
+    L = q.shape[0]
+    dq = np.zeros_like(q)
+    drho = np.zeros_like(rho)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dg = 0.0
+    for s0 in range(0, L, block):
+        r = np.arange(s0, min(s0 + block, L))
+        n = int(r[-1]) + 1
+        W, R, rbar, o_sa, corr, _ = _head_forward_blocks(q, k, v, rho, g, scale, r, n)
+        do = dout[r]
+        o = o_sa - g * corr
+        Delta = do @ v[:n].T
+        D = (do * o_sa).sum(axis=1, keepdims=True)
+        F = (do * o).sum(axis=1, keepdims=True)
+        Rc = R - rbar
+        dv[:n] += (W * (1.0 - g * Rc)).T @ do
+        dR = -g * W * (Delta - D)
+        dS = W * (Delta * (1.0 - g * Rc) + g * Rc * D - F)
+        dq[r] = scale * (dS @ k[:n])
+        drho[r] = dR @ k[:n]
+        dk[:n] += scale * (dS.T @ q[r]) + dR.T @ rho[r]
+        dg -= float((do * corr).sum())
+    return dq, dk, dv, drho, dg
+
+
+def prefill_backward(q, k, v, rho, gate, dout, scale=None, heads=None):
+    """Gradients of sum(out * dout) for the causal prefill.  Returns
+    dict(dq, dk, dv, drho [B,H,L,d], dgate [H]).  With `heads`, only those
+    (b, h) pairs are computed (their rows of the other arrays stay NaN) and
+    dgate sums their contributions only."""
+    q, k, v, rho, gate, dout = map(_f64, (q, k, v, rho, gate, dout))
+    B, H, L, dk_ = q.shape
+    sc = _default_scale(dk_, scale)
+    res = {n: np.full(q.shape if n != "dv" else v.shape, np.nan)
+           for n in ("dq", "dk", "dv", "drho")}
+    res["dgate"] = np.zeros(H)
+    todo = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b, h in todo:
+        g = prefill_head_backward(q[b, h], k[b, h], v[b, h], rho[b, h], gate[h], sc,
+                                  dout[b, h])
+        res["dq"][b, h], res["dk"][b, h], res["dv"][b, h], res["drho"][b, h] = g[:4]
+        res["dgate"][h] += g[4]
+    return res
