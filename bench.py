@@ -16,6 +16,10 @@ decode block carries its own for the split-KV kernel.
 
 Unless --no-extra is given, the two other full-size workloads (long ragged
 decode and the d=64 prefill) are timed too and reported under "extra".
+"backward" times the training forward pass (which also saves the statistics
+the gradient needs) and the backward pass on the prefill workloads; its
+TFLOP/s count 16*d flops per causal pair (S and R recomputed, dO V^T, and the
+dV, dK (two), dQ and drho products), twice the forward's 8*d.
 "softmax_relative" times the same kernels with the correction branch compiled
 out (plain causal softmax attention) against the Parallax kernels on each
 workload, alternating the two launch by launch, and reports the time ratio.
@@ -164,6 +168,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-softmax", action="store_true",
                     help="skip the timing against the softmax-only kernels")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the training forward and backward timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size kernel for scaling HBM byte counters)")
@@ -274,14 +280,20 @@ def main():
         res["calib_copy_bytes"] = {"read": n * 4, "write": n * 4}
         del src, dst
 
+    if not args.no_backward:
+        log("backward: workload 2")
+        res["backward"] = [backward_block(torch, plx, wl, pin, wp)]
     rel = []
     if not args.no_softmax:
         log("softmax-relative timing: workloads 2 and 3")
         rel.append(softmax_relative_prefill(torch, plx, wl, pin, wp, vt, pout))
         rel.append(softmax_relative_decode(torch, plx, wl, din, wd))
     if not args.no_extra:
-        res["extra"], rel_extra = extra_workloads(torch, plx, wl, dev,
-                                                  softmax=not args.no_softmax)
+        res["extra"], rel_extra, bwd_extra = extra_workloads(torch, plx, wl, dev,
+                                                             softmax=not args.no_softmax,
+                                                             backward=not args.no_backward)
+        if bwd_extra:
+            res["backward"].append(bwd_extra)
         rel += rel_extra
     if rel:
         res["softmax_relative"] = rel
@@ -291,6 +303,44 @@ def main():
         res["cpu_baseline"] = cpu_baseline_prefill(pin, wp)
         res["decode"]["cpu_baseline"] = cpu_baseline_decode(din, wd)
     print(json.dumps(res), flush=True)
+
+
+def backward_block(torch, plx, wl, inp, w, steps=10):
+    """Training forward pass and backward pass on one prefill workload, with a
+    seeded N(0,1) dout; all buffers allocated before timing."""
+    B, H, L, d = w.B, w.H, w.L, w.d
+    dev = inp["q"].device
+    g = torch.Generator(device=dev).manual_seed(1234)
+    dout = torch.randn((B, H, L, d), generator=g, device=dev, dtype=torch.float32)
+    fws = torch.empty(plx.prefill_workspace_bytes(B, H, L, d), dtype=torch.uint8, device=dev)
+    bws = torch.empty(plx.prefill_backward_workspace_bytes(B, H, L, d), dtype=torch.uint8,
+                      device=dev)
+    grads = tuple(torch.empty((B, H, L, d), dtype=torch.float32, device=dev) for _ in range(4)) \
+        + (torch.empty(H, dtype=torch.float32, device=dev),)
+    saved = {}
+
+    def fwd():
+        saved["t"] = plx.prefill_train(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"],
+                                       workspace=fws)
+
+    def bwd():
+        out, lse, rbar, corr = saved["t"]
+        plx.prefill_backward(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"], out, corr,
+                             lse, rbar, dout, grads=grads, workspace=bws)
+
+    tm = Timer(torch)
+    for _ in range(steps + 2):
+        tm.run("fwd", fwd)
+        tm.run("bwd", bwd)
+    torch.cuda.synchronize()
+    f_ms, b_ms = tm.ms("fwd", 2), tm.ms("bwd", 2)
+    fl = wl.prefill_flops(B, H, L, d)
+    return {"workload": w.name, "train_forward_ms": round(f_ms, 4),
+            "backward_ms": round(b_ms, 4), "step_ms": round(f_ms + b_ms, 4),
+            "train_forward_TFLOP/s": round(fl / f_ms / 1e9, 2),
+            "backward_TFLOP/s": round(2 * fl / b_ms / 1e9, 2),
+            "backward_frac_of_mfma_peak": round(2 * fl / b_ms / 1e9 / PEAK_MFMA_BF16_TFLOPS, 4),
+            "flops": {"forward": fl, "backward": 2 * fl}}
 
 
 def softmax_relative_prefill(torch, plx, wl, inp, w, vt, pout, steps=10):
@@ -342,9 +392,9 @@ def softmax_relative_decode(torch, plx, wl, inp, w, steps=10):
             "bytes": {"parallax": nb, "softmax": nb_sm}}
 
 
-def extra_workloads(torch, plx, wl, dev, steps=10, softmax=True):
+def extra_workloads(torch, plx, wl, dev, steps=10, softmax=True, backward=True):
     """Long ragged decode (B8 H16, 65536..131072 keys) and the d=64 prefill."""
-    out, rel = [], []
+    out, rel, bwd = [], [], None
     w4 = wl.WORKLOADS[4]
     log("extra: decode workload 4")
     din = wl.make_workload(4, device=dev)
@@ -395,9 +445,13 @@ def extra_workloads(torch, plx, wl, dev, steps=10, softmax=True):
     if softmax:
         log("softmax-relative timing: workload 5")
         rel.append(softmax_relative_prefill(torch, plx, wl, pin, w5, vt, pout))
-    del pin, vt, pout
+    del vt, pout
+    if backward:
+        log("backward: workload 5")
+        bwd = backward_block(torch, plx, wl, pin, w5)
+    del pin
     torch.cuda.empty_cache()
-    return out, rel
+    return out, rel, bwd
 
 
 if __name__ == "__main__":

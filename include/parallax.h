@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 2
+#define PARALLAX_ABI_VERSION 3
 
 typedef enum {
   PLX_OK = 0,
@@ -178,6 +178,44 @@ int parallax_softmax_decode(const void* q, const void* kcache, const void* vcach
                             const int32_t* seqlens, int B, int H, int Lmax, int d, float scale,
                             int dtype, int split_keys, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/* ----------------------------------------------------------------- training
+ * The pages describe the forward pass only; pretraining (section "Results")
+ * needs its gradient.  These calls give the exact derivative of Eq. 2 of the
+ * causal prefill with respect to q, k, v, rho and the per-head gate, for
+ * PLX_BF16 inputs (PLX_F32 returns PLX_EUNSUPPORTED).
+ *
+ * parallax_prefill_train: parallax_prefill that also writes, per row,
+ *   lse  : [B, H, L] fp32, natural log of sum_j exp(scale <q_i,k_j>), j <= i
+ *   rbar : [B, H, L] fp32, sum_j w_ij <rho_i,k_j>
+ *   corr : [B, H, L, d] fp32, the correction Sigma^(i) rho_i
+ *          (out = o^SA - gate[h] * corr).
+ * out alone does not determine o^SA when the gate is non-zero, so the
+ * backward pass needs corr.  Workspace: parallax_prefill_workspace_bytes().
+ *
+ * parallax_prefill_backward: given out, corr, lse and rbar from
+ * parallax_prefill_train on the same inputs, and dout = dL/dout ([B,H,L,d]
+ * fp32), writes the gradients of L:
+ *   dq, dk, dv, drho : [B, H, L, d] fp32
+ *   dgate            : [H] fp32, summed over the batch
+ * Every output element is written; nothing is accumulated into the outputs.
+ * dout is rounded to bf16 for the matrix products (as are the softmax-weight
+ * gradients); all sums are fp32.  The result is deterministic (no atomics).
+ * Workspace: at least parallax_prefill_backward_workspace_bytes() bytes
+ * (about 5 * B*H*L*d*2 bytes), or NULL to let the library allocate on `stream`. */
+int parallax_prefill_train(const void* q, const void* k, const void* v, const void* rho,
+                           const float* gate, float* out, float* lse, float* rbar, float* corr,
+                           int B, int H, int L, int d, float scale, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+size_t parallax_prefill_backward_workspace_bytes(int B, int H, int L, int d);
+
+int parallax_prefill_backward(const void* q, const void* k, const void* v, const void* rho,
+                              const float* gate, const float* out, const float* corr,
+                              const float* lse, const float* rbar, const float* dout,
+                              float* dq, float* dk, float* dv, float* drho, float* dgate,
+                              int B, int H, int L, int d, float scale, int dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,8 @@ Language Modeling", section "Core mechanism", Eq. 2) is
 softmax attention minus a gated correction: the softmax-weighted covariance of
 values and keys applied to the probe rho_i.  `prefill` runs the causal forward
 pass over whole sequences; `decode` runs one query per sequence against a KV
-cache.  The `softmax_*` functions run the same kernels with the correction
+cache.  `prefill_train` and `prefill_backward` give the exact gradients of
+the causal prefill (bf16).  The `softmax_*` functions run the same kernels with the correction
 branch compiled out (plain causal softmax attention), the like-for-like
 baseline for the cost of the correction.  All are thin wrappers over the C ABI
 of libparallax.so: they check shapes, allocate outputs and workspaces with torch
@@ -25,7 +26,8 @@ from ._native import PLX_BF16, PLX_F32, ParallaxError, call, lib  # noqa: F401
 __all__ = ["prefill", "decode", "prefill_stage_v", "prefill_attend", "decode_partials",
            "decode_combine", "prefill_workspace_bytes", "decode_workspace_bytes",
            "decode_default_split", "softmax_prefill", "softmax_prefill_attend",
-           "softmax_decode", "ParallaxError"]
+           "softmax_decode", "prefill_train", "prefill_backward",
+           "prefill_backward_workspace_bytes", "ParallaxError"]
 
 _DT = {torch.bfloat16: PLX_BF16, torch.float32: PLX_F32}
 
@@ -131,6 +133,59 @@ def softmax_prefill(q, k, v, scale=None, out=None, workspace=None):
     _launch(q.device, "parallax_softmax_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(out),
             B, H, L, d, _scale(scale, d), _DT[dt], _ptr(workspace), wsb)
     return out
+
+
+def prefill_backward_workspace_bytes(B, H, L, d) -> int:
+    return int(lib().parallax_prefill_backward_workspace_bytes(B, H, L, d))
+
+
+def prefill_train(q, k, v, rho, gate, scale=None, workspace=None):
+    """Training forward pass (bf16): returns (out, lse, rbar, corr), the output
+    and the statistics prefill_backward needs: lse [B,H,L] natural-log
+    partition function, rbar [B,H,L], corr [B,H,L,d] = Sigma rho."""
+    B, H, L, d, dt = _prefill_checks(q, (("k", k), ("v", v), ("rho", rho)))
+    if dt != torch.bfloat16:
+        raise TypeError("prefill_train supports bfloat16 inputs only")
+    _check("gate", gate, torch.float32, (H,), q.device)
+    out, workspace, wsb = _prefill_out_ws(q, None, workspace)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    rbar = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    corr = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
+    _launch(q.device, "parallax_prefill_train", _ptr(q), _ptr(k), _ptr(v), _ptr(rho), _ptr(gate),
+            _ptr(out), _ptr(lse), _ptr(rbar), _ptr(corr), B, H, L, d, _scale(scale, d),
+            PLX_BF16, _ptr(workspace), wsb)
+    return out, lse, rbar, corr
+
+
+def prefill_backward(q, k, v, rho, gate, out, corr, lse, rbar, dout, scale=None, grads=None,
+                     workspace=None):
+    """Gradients of sum(out * dout) for the causal prefill (bf16 inputs).  out,
+    corr, lse and rbar come from prefill_train on the same inputs; dout is fp32
+    [B,H,L,d].  Returns (dq, dk, dv, drho [B,H,L,d] fp32, dgate [H] fp32)."""
+    B, H, L, d, dt = _prefill_checks(q, (("k", k), ("v", v), ("rho", rho)))
+    if dt != torch.bfloat16:
+        raise TypeError("prefill_backward supports bfloat16 inputs only")
+    _check("gate", gate, torch.float32, (H,), q.device)
+    for n, t in (("out", out), ("corr", corr), ("dout", dout)):
+        _check(n, t, torch.float32, (B, H, L, d), q.device)
+    for n, t in (("lse", lse), ("rbar", rbar)):
+        _check(n, t, torch.float32, (B, H, L), q.device)
+    if grads is None:
+        grads = tuple(torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
+                      for _ in range(4)) + (torch.empty(H, dtype=torch.float32, device=q.device),)
+    for n, t in zip(("dq", "dk", "dv", "drho"), grads[:4]):
+        _check(n, t, torch.float32, (B, H, L, d), q.device)
+    _check("dgate", grads[4], torch.float32, (H,), q.device)
+    wsb = prefill_backward_workspace_bytes(B, H, L, d)
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+    _check("workspace", workspace, device=q.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _launch(q.device, "parallax_prefill_backward", _ptr(q), _ptr(k), _ptr(v), _ptr(rho),
+            _ptr(gate), _ptr(out), _ptr(corr), _ptr(lse), _ptr(rbar), _ptr(dout),
+            *(_ptr(t) for t in grads), B, H, L, d, _scale(scale, d), PLX_BF16,
+            _ptr(workspace), wsb)
+    return grads
 
 
 def prefill_stage_v(v, vt=None):

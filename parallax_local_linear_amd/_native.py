@@ -39,6 +39,9 @@ SIGNATURES = {
     "parallax_softmax_prefill_attend": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp]),
     "parallax_softmax_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp,
                                      _sz, _vp]),
+    "parallax_prefill_train": (_i, [_vp] * 9 + [_i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "parallax_prefill_backward_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "parallax_prefill_backward": (_i, [_vp] * 15 + [_i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
 }
 
 _lib = None

@@ -25,6 +25,17 @@ hipError_t launch_decode_split(const void* q, const void* kc, const void* vc, co
 hipError_t launch_decode_combine(const float* part, const float* gate, const int* seqlens,
                                  float* out, int B, int H, int Lmax, int d, int C, bool corr,
                                  hipStream_t s);
+hipError_t launch_prefill_bf16_train(const void* q, const void* k, const void* vt,
+                                     const void* rho, const float* gate, float* out,
+                                     float* lse, float* rbar, float* corr, int B, int H, int L,
+                                     int d, float scale, hipStream_t s);
+hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, const void* rho,
+                                   const float* gate, const float* out, const float* corr,
+                                   const float* lse, const float* rbar, const float* dout,
+                                   float* dq, float* dk, float* dv, float* drho, float* dgate,
+                                   int B, int H, int L, int d, float scale, void* ws,
+                                   hipStream_t s);
+size_t bwd_workspace_bytes(int B, int H, int L, int d);
 }  // namespace plx
 
 namespace {
@@ -322,6 +333,63 @@ int parallax_softmax_prefill_attend(const void* q, const void* k, const void* vt
                                     int B, int H, int L, int d, float scale, void* stream) {
   return attend_impl("parallax_softmax_prefill_attend", q, k, vt16, nullptr, nullptr, out, B,
                      H, L, d, scale, (hipStream_t)stream, false);
+}
+
+size_t parallax_prefill_backward_workspace_bytes(int B, int H, int L, int d) {
+  if (B <= 0 || H <= 0 || L <= 0 || (d != 64 && d != 128)) return 0;
+  if ((long long)B * H * (long long)L * d > kMaxElems) return 0;
+  return plx::bwd_workspace_bytes(B, H, L, d);
+}
+
+int parallax_prefill_train(const void* q, const void* k, const void* v, const void* rho,
+                           const float* gate, float* out, float* lse, float* rbar, float* corr,
+                           int B, int H, int L, int d, float scale, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const char* fn = "parallax_prefill_train";
+  int st = PLX_OK;
+  if (!dims_ok(B, H, L, d, fn, "L", &st)) return st;
+  if (!dtype_ok(dtype, fn, &st)) return st;
+  if (dtype != PLX_BF16) return fail(PLX_EUNSUPPORTED, "%s: only PLX_BF16 is supported", fn);
+  if (!q || !k || !v || !rho || !gate || !out || !lse || !rbar || !corr)
+    return fail(PLX_EINVAL, "%s: null pointer", fn);
+  hipStream_t s = (hipStream_t)stream;
+  Scratch scratch;
+  void* ws = nullptr;
+  if (!get_workspace(workspace, workspace_bytes, vt_bytes(B, H, L, d), s, &scratch, &ws, fn, &st))
+    return st;
+  hipError_t e = plx::launch_stage_v(v, ws, B * H, L, d, s);
+  if (e != hipSuccess) return launch_fail(fn, "stage_v", e);
+  e = plx::launch_prefill_bf16_train(q, k, ws, rho, gate, out, lse, rbar, corr, B, H, L, d,
+                                     eff_scale(scale, d), s);
+  if (e != hipSuccess) return launch_fail(fn, "attend", e);
+  return ok();
+}
+
+int parallax_prefill_backward(const void* q, const void* k, const void* v, const void* rho,
+                              const float* gate, const float* out, const float* corr,
+                              const float* lse, const float* rbar, const float* dout, float* dq,
+                              float* dk, float* dv, float* drho, float* dgate, int B, int H,
+                              int L, int d, float scale, int dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  const char* fn = "parallax_prefill_backward";
+  int st = PLX_OK;
+  if (!dims_ok(B, H, L, d, fn, "L", &st)) return st;
+  if (!dtype_ok(dtype, fn, &st)) return st;
+  if (dtype != PLX_BF16) return fail(PLX_EUNSUPPORTED, "%s: only PLX_BF16 is supported", fn);
+  if (!q || !k || !v || !rho || !gate || !out || !corr || !lse || !rbar || !dout || !dq || !dk ||
+      !dv || !drho || !dgate)
+    return fail(PLX_EINVAL, "%s: null pointer", fn);
+  hipStream_t s = (hipStream_t)stream;
+  Scratch scratch;
+  void* ws = nullptr;
+  if (!get_workspace(workspace, workspace_bytes, plx::bwd_workspace_bytes(B, H, L, d), s,
+                     &scratch, &ws, fn, &st))
+    return st;
+  hipError_t e = plx::launch_prefill_backward(q, k, v, rho, gate, out, corr, lse, rbar, dout, dq,
+                                              dk, dv, drho, dgate, B, H, L, d,
+                                              eff_scale(scale, d), ws, s);
+  if (e != hipSuccess) return launch_fail(fn, "backward", e);
+  return ok();
 }
 
 int parallax_softmax_decode(const void* q, const void* kcache, const void* vcache, float* out,

@@ -1,0 +1,649 @@
+// Backward pass of the causal Parallax prefill in bf16 on CDNA4 matrix cores.
+//
+// The pages (page "Parallax - Parameterized Local Linear Attention for Language
+// Modeling") describe the forward pass only (section "Core mechanism", Eq. 2);
+// the backward pass is its exact derivative.  With S = scale Q K^T (causal),
+// W = rowsoftmax(S), R = rho K^T, rbar = rowsum(W*R), the correction
+// C = (W*R) V - (W V) rbar and O = W V - g C, the gradients of sum(O * dO) are
+//     Delta = dO V^T,  D = rowsum(dO * (O + g C)),  F = rowsum(dO * O)
+//     dV   = (W * (1 - g (R - rbar)))^T dO
+//     dR   = g W * (D - Delta)
+//     dS'  = scale W * (Delta * (1 - g (R - rbar)) + g (R - rbar) D - F)
+//     dQ   = dS' K,   dK = dS'^T Q + dR^T rho,   drho = dR K
+//     dg   = -sum over rows of <dO, C>
+// W is recomputed from the scores and the saved log partition function; rbar
+// and C come from the training forward pass.
+//
+// Kernels (one stream, in this order):
+//   bwd_prep_kernel   dO -> bf16 (row-major copy), per-row statistics
+//                     {lse*log2e, rbar, D, F} and per-tile partials of <dO, C>.
+//   stage_v_kernel    (bf16 output) transposed 64-row tiles of dO, Q, rho and K
+//                     with the rows of each 32-row group in the order in which a
+//                     lane group of the score MFMAs produces them.
+//   bwd_dkdv_kernel   key-stationary: a workgroup owns 16*KB*NW keys, each wave
+//                     16*KB of them with their K and V fragments in registers;
+//                     it streams the later queries through LDS in steps of 32
+//                     and accumulates dK^T and dV^T on the matrix cores.
+//   bwd_dq_kernel     query-stationary: a workgroup owns 16*NW queries (16 per
+//                     wave), streams the causal key range through LDS in tiles
+//                     of 64 and accumulates dQ^T and drho^T.
+//   bwd_dgate_kernel  sums the <dO, C> partials per head in a fixed order.
+// Both main kernels recompute S, R and Delta (three products) and add two or
+// three more, so no gradient needs atomics and the result is deterministic.
+// The elementwise products W~, dS' and dR are rounded to bf16 for the second
+// set of MFMAs, as are dO and every input; all sums are fp32.
+
+#include <type_traits>
+
+#include "plx_common.h"
+
+namespace plx {
+
+constexpr int BW_T = 64;    // rows per staged transposed tile (the forward's tile)
+constexpr int BW_BQ = 32;   // queries per step of the key-stationary kernel
+
+// Launch shapes (waves per workgroup, 16-key blocks per wave), per head dimension.
+#ifndef PLX_BW_KV_NW_D128
+#define PLX_BW_KV_NW_D128 4
+#endif
+#ifndef PLX_BW_KV_KB_D128
+#define PLX_BW_KV_KB_D128 2
+#endif
+#ifndef PLX_BW_KV_NW_D64
+#define PLX_BW_KV_NW_D64 4
+#endif
+#ifndef PLX_BW_KV_KB_D64
+#define PLX_BW_KV_KB_D64 2
+#endif
+#ifndef PLX_BW_Q_NW_D128
+#define PLX_BW_Q_NW_D128 8
+#endif
+#ifndef PLX_BW_Q_NW_D64
+#define PLX_BW_Q_NW_D64 8
+#endif
+
+// Row-major tile of `rows` rows of D bf16 features; 16-byte chunks XOR-swizzled
+// by row (conflict-free fragment reads, as in the forward kernel).
+template <int D>
+__device__ __forceinline__ int rm_off(int r, int c) {
+  return r * D + ((c ^ (r & (D / 8 - 1))) << 3);
+}
+// Transposed tile, one row of W positions per feature (W = 64 or 32).  For
+// W = 64 the chunk swizzle is the forward's V^T swizzle; for W = 32 a row holds
+// four chunks and rows f and f+4 must land in different bank quads.
+template <int W>
+__device__ __forceinline__ int tr_off(int f, int c) {
+  if constexpr (W == 64) return f * 64 + ((c ^ (f & 7)) << 3);
+  else return f * 32 + ((c ^ ((f >> 2) & 3)) << 3);
+}
+
+// ------------------------------------------------------------------- prep
+// Four threads per row, 64 rows per workgroup.
+template <int D>
+__global__ __launch_bounds__(256)
+void bwd_prep_kernel(const float* __restrict__ dout, const float* __restrict__ out,
+                     const float* __restrict__ corr, const float* __restrict__ lse,
+                     const float* __restrict__ rbar, const float* __restrict__ gate,
+                     __bf16* __restrict__ do16, f32x4* __restrict__ stats,
+                     float* __restrict__ gpart, int H, int L, int n_t) {
+  constexpr int PER = D / 4;
+  __shared__ float red[4];
+  const int bh = blockIdx.x / n_t, t = blockIdx.x % n_t;
+  const int h = bh % H;
+  const int tid = threadIdx.x;
+  const int row = t * 64 + (tid >> 2);
+  const int part = tid & 3;
+  float fo = 0.f, fc = 0.f, gx = 0.f;
+  if (row < L) {
+    const size_t base = ((size_t)bh * L + row) * D + part * PER;
+#pragma unroll
+    for (int c = 0; c < PER; c += 8) {
+      bf16x8 pk;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 dx = *reinterpret_cast<const f32x4*>(dout + base + c + 4 * hf);
+        const f32x4 ox = *reinterpret_cast<const f32x4*>(out + base + c + 4 * hf);
+        const f32x4 cx = *reinterpret_cast<const f32x4*>(corr + base + c + 4 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const __bf16 b = (__bf16)dx[e];
+          const float dr = (float)b;
+          pk[4 * hf + e] = b;
+          fo = fmaf(dr, ox[e], fo);
+          fc = fmaf(dr, cx[e], fc);
+          gx = fmaf(dx[e], cx[e], gx);
+        }
+      }
+      *reinterpret_cast<bf16x8*>(do16 + base + c) = pk;
+    }
+  }
+  fo = group_sum<4>(fo);
+  fc = group_sum<4>(fc);
+  gx = group_sum<4>(gx);
+  if (row < L && part == 0) {
+    // D uses o_sa = o + g C; both D and F come from the rounded dO that the
+    // products Delta = dO V^T see, so that the dS rows sum to zero
+    stats[(size_t)bh * L + row] =
+        f32x4{lse[(size_t)bh * L + row] * kLog2e, rbar[(size_t)bh * L + row],
+              fmaf(gate[h], fc, fo), fo};
+  }
+  // tile partial of sum <dO, C> (exact fp32 dO), lanes then waves in a fixed order
+  float x = (part == 0 && row < L) ? gx : 0.f;
+  x = group_sum<32>(x);
+  x += __shfl_xor(x, 32);
+  if ((tid & 63) == 0) red[tid >> 6] = x;
+  __syncthreads();
+  if (tid == 0) gpart[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// dgate[h] = -sum over b and tiles of the partials, one thread per head.
+__global__ __launch_bounds__(64)
+void bwd_dgate_kernel(const float* __restrict__ gpart, float* __restrict__ dgate, int B, int H,
+                      int n_t) {
+  const int h = blockIdx.x * 64 + threadIdx.x;
+  if (h >= H) return;
+  float s = 0.f;
+  for (int b = 0; b < B; ++b)
+    for (int t = 0; t < n_t; ++t) s += gpart[((size_t)b * H + h) * n_t + t];
+  dgate[h] = -s;
+}
+
+// Elementwise step shared by both main kernels, for one (query, key) score:
+// returns W~ = w (1 - g rc), dS' and dR.
+struct BwdElt {
+  float wt, ds, dr;
+};
+__device__ __forceinline__ BwdElt bwd_elt(bool keep, float s, float r, float dl, f32x4 st,
+                                          float g, float sl2, float scale) {
+  // st = {lse*log2e, rbar, D, F}; a masked score contributes exact zeros
+  const float w = keep ? __builtin_amdgcn_exp2f(fmaf(s, sl2, -st[0])) : 0.f;
+  const float rc = r - st[1];
+  const float t1 = fmaf(-g, rc, 1.f);
+  BwdElt e;
+  e.wt = w * t1;
+  e.ds = (w * scale) * (fmaf(dl, t1, g * rc * st[2]) - st[3]);
+  e.dr = (g * w) * (st[2] - dl);
+  return e;
+}
+
+// ------------------------------------------------------- key-stationary dK, dV
+template <int D, int NW, int KB>
+__global__ __launch_bounds__(64 * NW, 1)
+void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                     const __bf16* __restrict__ v, const __bf16* __restrict__ rho,
+                     const __bf16* __restrict__ do16, const __bf16* __restrict__ qT,
+                     const __bf16* __restrict__ rT, const __bf16* __restrict__ dT,
+                     const f32x4* __restrict__ stats, const float* __restrict__ gate,
+                     float* __restrict__ dk, float* __restrict__ dv, int H, int L, int BH,
+                     int n_kblk, float sl2, float scale) {
+  constexpr int KSTEPS = D / 32;
+  constexpr int FB = D / 16;
+  constexpr int BK = 16 * KB * NW;                 // keys per workgroup
+  constexpr int RM = BW_BQ * D;                    // elements of a row-major step tile
+  constexpr int TR = D * BW_BQ;                    // elements of a transposed step tile
+  constexpr int STAGE = 3 * RM + 3 * TR + 64 * 8;  // + 64 stats records (1 KB)
+  constexpr int RMBLK = RM * 2 / 1024;             // 1-KB blocks per tile
+  static_assert(RMBLK % NW == 0, "tile blocks per wave");
+  __shared__ __align__(16) uint16_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int kblk = (int)(blockIdx.x / (unsigned)BH);   // lowest key blocks (most work) first
+  const int bh = (int)(blockIdx.x % (unsigned)BH);
+  const int h = bh % H;
+  const int k0 = kblk * BK;
+  const int kw0 = k0 + 16 * KB * wave;
+  const size_t head = (size_t)bh * L * D;
+  const int n64 = (L + BW_T - 1) / BW_T;
+  const float g = gate[h];
+
+  // B-operand fragments of this wave's keys: key kw0 + 16 kb + c16, features
+  // 32 kk + 8 g4 .. +7
+  bf16x8 kf[KB][KSTEPS], vf[KB][KSTEPS];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int key = kw0 + 16 * kb + c16;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      if (key < L) {
+        kf[kb][kk] = *reinterpret_cast<const bf16x8*>(k + head + (size_t)key * D + 32 * kk + 8 * g4);
+        vf[kb][kk] = *reinterpret_cast<const bf16x8*>(v + head + (size_t)key * D + 32 * kk + 8 * g4);
+      } else {
+        kf[kb][kk] = bf16x8{};
+        vf[kb][kk] = bf16x8{};
+      }
+    }
+  }
+  f32x4 dk_acc[KB][FB], dv_acc[KB][FB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb) {
+      dk_acc[kb][fb] = f32x4{};
+      dv_acc[kb][fb] = f32x4{};
+    }
+  }
+
+  // per-lane byte offsets of this wave's 1-KB blocks (swizzle included)
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t rmoff[RMBLK / NW], troff[RMBLK / NW];
+#pragma unroll
+  for (int i = 0; i < RMBLK / NW; ++i) {
+    const int e = (i * NW + wave) * 512 + 8 * lane;
+    {
+      const int r = e / D, pc = (e % D) / 8;
+      rmoff[i] = (uint32_t)((r * D + ((pc ^ (r & (D / 8 - 1))) << 3)) * 2);
+    }
+    {
+      const int f = e / BW_BQ, pc = (e % BW_BQ) / 8;
+      // logical chunk c sits at physical chunk c ^ ((f >> 2) & 3); the global
+      // tile row of feature f holds 64 positions, this step's 32 start at
+      // the half selected by the base pointer
+      troff[i] = (uint32_t)((f * BW_T + ((pc ^ ((f >> 2) & 3)) << 3)) * 2);
+    }
+  }
+  const int n_qs = (L + BW_BQ - 1) / BW_BQ;
+  const int qs0 = k0 / BW_BQ;
+  auto load_stage = [&](int qs, int buf) {
+    uint16_t* st = smem + buf * STAGE;
+    const int q0 = qs * BW_BQ;
+    const int rows = min(BW_BQ, L - q0);
+    const size_t roff = head + (size_t)q0 * D;
+    const __bf16* srcs[3] = {q + roff, rho + roff, do16 + roff};
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+#pragma unroll
+      for (int i = 0; i < RMBLK / NW; ++i)
+        buffer_load_lds16(srcs[m], rows * D * 2, st + m * RM + (i * NW + wave_u) * 512, rmoff[i]);
+    }
+    // transposed tiles: staged [bh][n64][D][64], this step is half (qs & 1)
+    const size_t toff = ((size_t)bh * n64 + (qs >> 1)) * (size_t)(D * BW_T) + (qs & 1) * BW_BQ;
+    const __bf16* trs[3] = {qT + toff, rT + toff, dT + toff};
+    const int tbytes = (D * BW_T - (qs & 1) * BW_BQ) * 2;
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+#pragma unroll
+      for (int i = 0; i < RMBLK / NW; ++i)
+        buffer_load_lds16(trs[m], tbytes, st + 3 * RM + m * TR + (i * NW + wave_u) * 512,
+                          troff[i]);
+    }
+    // statistics of rows q0 .. q0+63 (the second half is not used)
+    if (wave_u == 0)
+      buffer_load_lds16(stats + (size_t)bh * L + q0, (L - q0) * 16, st + 3 * RM + 3 * TR,
+                        (uint32_t)(16 * lane));
+  };
+
+  auto compute = [&](int qs, int buf) {
+    const uint16_t* st = smem + buf * STAGE;
+    const uint16_t* Qs = st;
+    const uint16_t* Rs = st + RM;
+    const uint16_t* Os = st + 2 * RM;
+    const uint16_t* QTs = st + 3 * RM;
+    const uint16_t* RTs = st + 3 * RM + TR;
+    const uint16_t* OTs = st + 3 * RM + 2 * TR;
+    const f32x4* Ss = reinterpret_cast<const f32x4*>(st + 3 * RM + 3 * TR);
+    const int q0 = qs * BW_BQ;
+    // S = Q K^T, R = rho K^T, Delta = dO V^T for 32 queries x 16*KB keys; lane
+    // holds key kw0 + 16 kb + c16 and queries q0 + 16 qb + 4 g4 + j
+    f32x4 sa[KB][2], ra[KB][2], da[KB][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const int off = rm_off<D>(16 * qb + c16, 4 * kk + g4);
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qs + off);
+        const bf16x8 ar = *reinterpret_cast<const bf16x8*>(Rs + off);
+        const bf16x8 ao = *reinterpret_cast<const bf16x8*>(Os + off);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          if (kk == 0) {
+            sa[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kf[kb][0], f32x4{}, 0, 0, 0);
+            ra[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, kf[kb][0], f32x4{}, 0, 0, 0);
+            da[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, vf[kb][0], f32x4{}, 0, 0, 0);
+          } else {
+            sa[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kf[kb][kk], sa[kb][qb], 0, 0, 0);
+            ra[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, kf[kb][kk], ra[kb][qb], 0, 0, 0);
+            da[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, vf[kb][kk], da[kb][qb], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // W~, dS', dR in bf16: element e = 4 qb + j of a key's 8 queries, the
+    // position order of the staged transposed tiles
+    bf16x8 wtp[KB], dsp[KB], drp[KB];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int qr = 16 * qb + 4 * g4 + j;
+        const f32x4 sv = Ss[qr];
+        const int qq = q0 + qr;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int key = kw0 + 16 * kb + c16;
+          const bool keep = qq >= key && qq < L;
+          const BwdElt el = bwd_elt(keep, sa[kb][qb][j], ra[kb][qb][j], da[kb][qb][j], sv, g,
+                                    sl2, scale);
+          wtp[kb][4 * qb + j] = (__bf16)el.wt;
+          dsp[kb][4 * qb + j] = (__bf16)el.ds;
+          drp[kb][4 * qb + j] = (__bf16)el.dr;
+        }
+      }
+    }
+    // dV^T += dO^T W~,  dK^T += Q^T dS' + rho^T dR
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb) {
+      const int off = tr_off<BW_BQ>(16 * fb + c16, g4);
+      const bf16x8 ao = *reinterpret_cast<const bf16x8*>(OTs + off);
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(QTs + off);
+      const bf16x8 ar = *reinterpret_cast<const bf16x8*>(RTs + off);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        dv_acc[kb][fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, wtp[kb], dv_acc[kb][fb], 0, 0, 0);
+        dk_acc[kb][fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, dsp[kb], dk_acc[kb][fb], 0, 0, 0);
+        dk_acc[kb][fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, drp[kb], dk_acc[kb][fb], 0, 0, 0);
+      }
+    }
+  };
+
+  if (qs0 < n_qs) {
+    load_stage(qs0, 0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  }
+  for (int qs = qs0; qs < n_qs; ++qs) {
+    const int buf = (qs - qs0) & 1;
+    // staging is unconditional: past the last step the loads re-read it into
+    // the buffer no wave reads again
+    load_stage(min(qs + 1, n_qs - 1), 1 - buf);
+    // a wave whose keys all follow the step's last query has nothing to add
+    if (qs * BW_BQ + BW_BQ - 1 >= kw0) compute(qs, buf);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int key = kw0 + 16 * kb + c16;
+    if (key < L) {
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        *reinterpret_cast<f32x4*>(dk + head + (size_t)key * D + 16 * fb + 4 * g4) = dk_acc[kb][fb];
+        *reinterpret_cast<f32x4*>(dv + head + (size_t)key * D + 16 * fb + 4 * g4) = dv_acc[kb][fb];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------- query-stationary dQ, drho
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 1)
+void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                   const __bf16* __restrict__ v, const __bf16* __restrict__ rho,
+                   const __bf16* __restrict__ do16, const __bf16* __restrict__ kT,
+                   const f32x4* __restrict__ stats, const float* __restrict__ gate,
+                   float* __restrict__ dq, float* __restrict__ drho, int H, int L, int BH,
+                   int n_qt, float sl2, float scale) {
+  constexpr int KSTEPS = D / 32;
+  constexpr int FB = D / 16;
+  constexpr int BR = 16 * NW;                      // queries per workgroup
+  constexpr int TE = BW_T * D;                     // elements of one 64-key tile
+  constexpr int STAGE = 3 * TE;                    // K, V (row-major) and K^T
+  constexpr int TBLK = TE * 2 / 1024;
+  static_assert(TBLK % NW == 0, "tile blocks per wave");
+  __shared__ __align__(16) uint16_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int qt = n_qt - 1 - (int)(blockIdx.x / (unsigned)BH);   // longest rows first
+  const int bh = (int)(blockIdx.x % (unsigned)BH);
+  const int h = bh % H;
+  const int q0 = qt * BR;
+  const int qw0 = q0 + wave * 16;
+  const int qi = qw0 + c16;
+  const size_t head = (size_t)bh * L * D;
+  const int n64 = (L + BW_T - 1) / BW_T;
+  const float g = gate[h];
+
+  bf16x8 qf[KSTEPS], rf[KSTEPS], df[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    if (qi < L) {
+      const size_t o = head + (size_t)qi * D + 32 * kk + 8 * g4;
+      qf[kk] = *reinterpret_cast<const bf16x8*>(q + o);
+      rf[kk] = *reinterpret_cast<const bf16x8*>(rho + o);
+      df[kk] = *reinterpret_cast<const bf16x8*>(do16 + o);
+    } else {
+      qf[kk] = bf16x8{};
+      rf[kk] = bf16x8{};
+      df[kk] = bf16x8{};
+    }
+  }
+  const f32x4 sv = (qi < L) ? stats[(size_t)bh * L + qi] : f32x4{};
+  f32x4 dq_acc[FB], dr_acc[FB];
+#pragma unroll
+  for (int fb = 0; fb < FB; ++fb) {
+    dq_acc[fb] = f32x4{};
+    dr_acc[fb] = f32x4{};
+  }
+
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t rmoff[TBLK / NW], troff[TBLK / NW];
+#pragma unroll
+  for (int i = 0; i < TBLK / NW; ++i) {
+    const int e = (i * NW + wave) * 512 + 8 * lane;
+    {
+      const int r = e / D, pc = (e % D) / 8;
+      rmoff[i] = (uint32_t)((r * D + ((pc ^ (r & (D / 8 - 1))) << 3)) * 2);
+    }
+    {
+      const int f = e / BW_T, pc = (e % BW_T) / 8;
+      troff[i] = (uint32_t)((f * BW_T + ((pc ^ (f & 7)) << 3)) * 2);
+    }
+  }
+  const int last_q = min(q0 + BR, L) - 1;
+  const int n_kt = last_q / BW_T + 1;
+  const int n_w = (qw0 < L) ? min(qw0 + 15, L - 1) / BW_T + 1 : 0;
+  auto load_stage = [&](int kt, int buf) {
+    uint16_t* st = smem + buf * STAGE;
+    const int rows = min(BW_T, L - kt * BW_T);
+    const size_t roff = head + (size_t)kt * BW_T * D;
+    const __bf16* srcs[2] = {k + roff, v + roff};
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int i = 0; i < TBLK / NW; ++i)
+        buffer_load_lds16(srcs[m], rows * D * 2, st + m * TE + (i * NW + wave_u) * 512, rmoff[i]);
+    }
+    const __bf16* kts = kT + ((size_t)bh * n64 + kt) * (size_t)(D * BW_T);
+#pragma unroll
+    for (int i = 0; i < TBLK / NW; ++i)
+      buffer_load_lds16(kts, TE * 2, st + 2 * TE + (i * NW + wave_u) * 512, troff[i]);
+  };
+
+  auto compute = [&](int kt, int buf, auto diag_c) {
+    const uint16_t* st = smem + buf * STAGE;
+    const uint16_t* Ks = st;
+    const uint16_t* Vs = st + TE;
+    const uint16_t* KTs = st + 2 * TE;
+    // S^T = K Q^T, R^T = K rho^T, Delta^T = V dO^T; lane holds query qi and
+    // keys kt*64 + 16 kb + 4 g4 + j
+    f32x4 sa[4], ra[4], da[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const int off = rm_off<D>(16 * kb + c16, 4 * kk + g4);
+        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(Ks + off);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(Vs + off);
+        if (kk == 0) {
+          sa[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, qf[0], f32x4{}, 0, 0, 0);
+          ra[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, rf[0], f32x4{}, 0, 0, 0);
+          da[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, df[0], f32x4{}, 0, 0, 0);
+        } else {
+          sa[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, qf[kk], sa[kb], 0, 0, 0);
+          ra[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, rf[kk], ra[kb], 0, 0, 0);
+          da[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, df[kk], da[kb], 0, 0, 0);
+        }
+      }
+    }
+    const int lim = qi - kt * BW_T - 4 * g4;   // key offset 16 kb + j is causal iff <= lim
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16x8 dsp, drp;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int kb = 2 * t + hh;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool keep = !decltype(diag_c)::value || (16 * kb + j <= lim);
+          const BwdElt el = bwd_elt(keep, sa[kb][j], ra[kb][j], da[kb][j], sv, g, sl2, scale);
+          dsp[4 * hh + j] = (__bf16)el.ds;
+          drp[4 * hh + j] = (__bf16)el.dr;
+        }
+      }
+      // dQ^T += K^T dS'^T,  drho^T += K^T dR^T over the 32 keys of group t
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(KTs + tr_off<BW_T>(16 * fb + c16, 4 * t + g4));
+        dq_acc[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dsp, dq_acc[fb], 0, 0, 0);
+        dr_acc[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, drp, dr_acc[fb], 0, 0, 0);
+      }
+    }
+  };
+
+  load_stage(0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    load_stage(min(kt + 1, n_kt - 1), 1 - buf);
+    if (kt < n_w) {
+      if (kt + 1 == n_w) compute(kt, buf, std::true_type{});
+      else compute(kt, buf, std::false_type{});
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  }
+
+  if (qi < L) {
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb) {
+      *reinterpret_cast<f32x4*>(dq + head + (size_t)qi * D + 16 * fb + 4 * g4) = dq_acc[fb];
+      *reinterpret_cast<f32x4*>(drho + head + (size_t)qi * D + 16 * fb + 4 * g4) = dr_acc[fb];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launches
+hipError_t launch_stage_t_bf16(const void* x, void* xt, int BH, int L, int d, hipStream_t s);
+
+// Scratch layout of one backward call, in bytes from the workspace start.
+struct BwdScratch {
+  size_t do16, dT, qT, rT, kT, stats, gpart, total;
+};
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+BwdScratch bwd_scratch(int B, int H, int L, int d) {
+  const size_t BH = (size_t)B * H;
+  const size_t n64 = (size_t)((L + BW_T - 1) / BW_T);
+  const size_t rm = align256(BH * L * d * 2);
+  const size_t tr = align256(BH * n64 * BW_T * d * 2);
+  BwdScratch w;
+  w.do16 = 0;
+  w.dT = w.do16 + rm;
+  w.qT = w.dT + tr;
+  w.rT = w.qT + tr;
+  w.kT = w.rT + tr;
+  w.stats = w.kT + tr;
+  w.gpart = w.stats + align256(BH * L * 16);
+  w.total = w.gpart + align256(BH * n64 * 4);
+  return w;
+}
+
+template <int D, int NW, int KB>
+static void launch_dkdv_t(const void* q, const void* k, const void* v, const void* rho,
+                          const void* do16, const void* qT, const void* rT, const void* dT,
+                          const void* stats, const float* gate, float* dk, float* dv, int BH,
+                          int H, int L, float sl2, float scale, hipStream_t s) {
+  constexpr int BK = 16 * KB * NW;
+  const int n_kblk = (L + BK - 1) / BK;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, KB>), dim3((unsigned)(BH * n_kblk)), dim3(64 * NW),
+                     0, s, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
+                     (const __bf16*)rho, (const __bf16*)do16, (const __bf16*)qT,
+                     (const __bf16*)rT, (const __bf16*)dT, (const f32x4*)stats, gate, dk, dv, H,
+                     L, BH, n_kblk, sl2, scale);
+}
+
+template <int D, int NW>
+static void launch_dq_t(const void* q, const void* k, const void* v, const void* rho,
+                        const void* do16, const void* kT, const void* stats, const float* gate,
+                        float* dq, float* drho, int BH, int H, int L, float sl2, float scale,
+                        hipStream_t s) {
+  const int n_qt = (L + 16 * NW - 1) / (16 * NW);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3((unsigned)(BH * n_qt)), dim3(64 * NW), 0, s,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)rho,
+                     (const __bf16*)do16, (const __bf16*)kT, (const f32x4*)stats, gate, dq, drho,
+                     H, L, BH, n_qt, sl2, scale);
+}
+
+hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, const void* rho,
+                                   const float* gate, const float* out, const float* corr,
+                                   const float* lse, const float* rbar, const float* dout,
+                                   float* dq, float* dk, float* dv, float* drho, float* dgate,
+                                   int B, int H, int L, int d, float scale, void* ws,
+                                   hipStream_t s) {
+  const int BH = B * H;
+  const int n64 = (L + BW_T - 1) / BW_T;
+  const BwdScratch w = bwd_scratch(B, H, L, d);
+  char* base = static_cast<char*>(ws);
+  void* do16 = base + w.do16;
+  void* dT = base + w.dT;
+  void* qT = base + w.qT;
+  void* rT = base + w.rT;
+  void* kT = base + w.kT;
+  f32x4* stats = reinterpret_cast<f32x4*>(base + w.stats);
+  float* gpart = reinterpret_cast<float*>(base + w.gpart);
+  const float sl2 = scale * kLog2e;
+
+  if (d == 128)
+    hipLaunchKernelGGL(bwd_prep_kernel<128>, dim3((unsigned)(BH * n64)), dim3(256), 0, s, dout,
+                       out, corr, lse, rbar, gate, (__bf16*)do16, stats, gpart, H, L, n64);
+  else
+    hipLaunchKernelGGL(bwd_prep_kernel<64>, dim3((unsigned)(BH * n64)), dim3(256), 0, s, dout,
+                       out, corr, lse, rbar, gate, (__bf16*)do16, stats, gpart, H, L, n64);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const void* srcs[4] = {do16, q, rho, k};
+  void* dsts[4] = {dT, qT, rT, kT};
+  for (int i = 0; i < 4; ++i) {
+    e = launch_stage_t_bf16(srcs[i], dsts[i], BH, L, d, s);
+    if (e != hipSuccess) return e;
+  }
+  if (d == 128) {
+    launch_dkdv_t<128, PLX_BW_KV_NW_D128, PLX_BW_KV_KB_D128>(q, k, v, rho, do16, qT, rT, dT,
+                                                              stats, gate, dk, dv, BH, H, L,
+                                                              sl2, scale, s);
+    launch_dq_t<128, PLX_BW_Q_NW_D128>(q, k, v, rho, do16, kT, stats, gate, dq, drho, BH, H, L,
+                                       sl2, scale, s);
+  } else {
+    launch_dkdv_t<64, PLX_BW_KV_NW_D64, PLX_BW_KV_KB_D64>(q, k, v, rho, do16, qT, rT, dT, stats,
+                                                          gate, dk, dv, BH, H, L, sl2, scale, s);
+    launch_dq_t<64, PLX_BW_Q_NW_D64>(q, k, v, rho, do16, kT, stats, gate, dq, drho, BH, H, L,
+                                     sl2, scale, s);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dgate_kernel, dim3((unsigned)((H + 63) / 64)), dim3(64), 0, s, gpart,
+                     dgate, B, H, n64);
+  return hipGetLastError();
+}
+
+size_t bwd_workspace_bytes(int B, int H, int L, int d) { return bwd_scratch(B, H, L, d).total; }
+
+}  // namespace plx

@@ -18,6 +18,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 // Word 3 of a raw (untyped, stride 0) buffer descriptor on gfx9-family parts.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 // s_waitcnt immediate for "vmcnt(0)" with expcnt and lgkmcnt left unconstrained

@@ -125,14 +125,19 @@ __host__ __device__ constexpr int vt_key_of_pos(int p) {
 // budget at 256 per lane and keeps every MFMA operand in VGPRs.
 // CORR = false compiles the covariance branch out (no R, T, A_r or c): plain
 // causal softmax attention through the same staging, tiling and schedule, the
-// baseline for the cost of the correction.
-template <int D, int NW, bool PIPE, bool CORR>
+// baseline for the cost of the correction.  SAVE = true (training) also writes
+// what the backward pass needs: the natural-log partition function of every
+// row, rbar = c / l and the correction vector (u - o_sa rbar).
+template <int D, int NW, bool PIPE, bool CORR, bool SAVE>
 __global__ __launch_bounds__(64 * NW, CORR ? (D == 64 ? PLX_PF_MINW_D64 : PLX_PF_MINW_D128)
                                           : (D == 64 ? PLX_SM_MINW_D64 : PLX_SM_MINW_D128))
 void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                          const _Float16* __restrict__ vt, const __bf16* __restrict__ rho,
                          const float* __restrict__ gate, float* __restrict__ out,
-                         int H, int L, int BH, int n_qt, float sl2) {
+                         float* __restrict__ lse_out, float* __restrict__ rbar_out,
+                         float* __restrict__ corr_out, int H, int L, int BH, int n_qt,
+                         float sl2) {
+  static_assert(CORR || !SAVE, "the training statistics belong to the Parallax kernel");
   using LY = PfLayout<D>;
   constexpr int PF_BR = 16 * NW;                         // queries per workgroup
   constexpr int PF_THREADS = 64 * NW;
@@ -444,17 +449,36 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         }
       }
       *reinterpret_cast<f32x4*>(orow + 16 * fb + 4 * g4) = o;
+      if constexpr (SAVE) {
+        f32x4 cv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float osa = acc_o[fb][j] * inv;
+          cv[j] = acc_r[fb][j] * inv - osa * rbar;
+        }
+        *reinterpret_cast<f32x4*>(corr_out + head + (size_t)qi * D + 16 * fb + 4 * g4) = cv;
+      }
+    }
+    if constexpr (SAVE) {
+      // l sums 2^(s*scale*log2e - m) over the row, so log2 of the partition
+      // function is m + log2(l); the four lanes of a query hold the same values
+      if (g4 == 0) {
+        lse_out[(size_t)bh * L + qi] = (m_run + __log2f(l_tot)) * kLn2;
+        rbar_out[(size_t)bh * L + qi] = rbar;
+      }
     }
   }
 }
 
-// V [BH, L, D] bf16 -> V^T tiles [BH][ceil(L/64)][D][64] fp16, zero past L, with the
-// keys of each 32-key group in vt_key_of_pos order.
-// One workgroup per (head, 64-key tile): coalesced 16-B loads into LDS, then
-// each thread gathers 8 keys of one feature, converts and stores 16 B.
-template <int D>
+// X [BH, L, D] bf16 -> X^T tiles [BH][ceil(L/64)][D][64] of TOUT (fp16 for the
+// forward's V^T, bf16 for the backward's transposed operands), zero past L, with
+// the rows of each 32-row group in vt_key_of_pos order.
+// One workgroup per (head, 64-row tile): coalesced 16-B loads into LDS, then
+// each thread gathers 8 rows of one feature, converts and stores 16 B.
+template <int D, typename TOUT>
 __global__ __launch_bounds__(256)
-void stage_v_kernel(const __bf16* __restrict__ v, _Float16* __restrict__ vt, int L, int n_kt) {
+void stage_v_kernel(const __bf16* __restrict__ v, TOUT* __restrict__ vt, int L, int n_kt) {
+  typedef TOUT outx8 __attribute__((ext_vector_type(8)));
   constexpr int PITCH = D + 2;     // odd dword pitch spreads the column reads over banks
   __shared__ uint16_t tile[PF_BC * PITCH];
   const int bh = blockIdx.x / n_kt;
@@ -470,41 +494,58 @@ void stage_v_kernel(const __bf16* __restrict__ v, _Float16* __restrict__ vt, int
     dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2]; dst[3] = w[3];
   }
   __syncthreads();
-  _Float16* dst = vt + ((size_t)bh * n_kt + kt) * (size_t)(D * PF_BC);
+  TOUT* dst = vt + ((size_t)bh * n_kt + kt) * (size_t)(D * PF_BC);
   for (int ch = tid; ch < CH; ch += 256) {
     const int f = ch / (PF_BC / 8), key0 = (ch % (PF_BC / 8)) * 8;
-    f16x8 o;
+    outx8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int key = vt_key_of_pos(key0 + e);
       const float x = __uint_as_float((uint32_t)tile[key * PITCH + f] << 16);
-      o[e] = (_Float16)x;
+      o[e] = (TOUT)x;
     }
-    *reinterpret_cast<f16x8*>(dst + (size_t)ch * 8) = o;
+    *reinterpret_cast<outx8*>(dst + (size_t)ch * 8) = o;
   }
 }
 
-hipError_t launch_stage_v(const void* v, void* vt, int BH, int L, int d, hipStream_t s) {
+template <typename TOUT>
+static hipError_t launch_stage_t(const void* v, void* vt, int BH, int L, int d, hipStream_t s) {
   const int n_kt = (L + PF_BC - 1) / PF_BC;
   const dim3 grid((unsigned)(BH * n_kt));
   if (d == 128)
-    hipLaunchKernelGGL(stage_v_kernel<128>, grid, dim3(256), 0, s, (const __bf16*)v,
-                       (_Float16*)vt, L, n_kt);
+    hipLaunchKernelGGL((stage_v_kernel<128, TOUT>), grid, dim3(256), 0, s, (const __bf16*)v,
+                       (TOUT*)vt, L, n_kt);
   else
-    hipLaunchKernelGGL(stage_v_kernel<64>, grid, dim3(256), 0, s, (const __bf16*)v,
-                       (_Float16*)vt, L, n_kt);
+    hipLaunchKernelGGL((stage_v_kernel<64, TOUT>), grid, dim3(256), 0, s, (const __bf16*)v,
+                       (TOUT*)vt, L, n_kt);
   return hipGetLastError();
 }
 
-template <int D, int NW, bool PIPE, bool CORR>
+hipError_t launch_stage_v(const void* v, void* vt, int BH, int L, int d, hipStream_t s) {
+  return launch_stage_t<_Float16>(v, vt, BH, L, d, s);
+}
+
+hipError_t launch_stage_t_bf16(const void* x, void* xt, int BH, int L, int d, hipStream_t s) {
+  return launch_stage_t<__bf16>(x, xt, BH, L, d, s);
+}
+
+// Pointers a training forward writes besides the output (all null otherwise).
+struct TrainOut {
+  float* lse;
+  float* rbar;
+  float* corr;
+};
+
+template <int D, int NW, bool PIPE, bool CORR, bool SAVE = false>
 static hipError_t launch_prefill_t(const void* q, const void* k, const void* vt,
                                    const void* rho, const float* gate, float* out, int B,
-                                   int H, int L, float sl2, hipStream_t s) {
+                                   int H, int L, float sl2, hipStream_t s, TrainOut tr = {}) {
   const int BH = B * H;
   const int n_qt = (L + 16 * NW - 1) / (16 * NW);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, PIPE, CORR>), dim3((unsigned)(BH * n_qt)), dim3(64 * NW),
-                     0, s, (const __bf16*)q, (const __bf16*)k, (const _Float16*)vt,
-                     (const __bf16*)rho, gate, out, H, L, BH, n_qt, sl2);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, PIPE, CORR, SAVE>), dim3((unsigned)(BH * n_qt)),
+                     dim3(64 * NW), 0, s, (const __bf16*)q, (const __bf16*)k,
+                     (const _Float16*)vt, (const __bf16*)rho, gate, out, tr.lse, tr.rbar,
+                     tr.corr, H, L, BH, n_qt, sl2);
   return hipGetLastError();
 }
 
@@ -527,6 +568,19 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* vt, con
   const float sl2 = scale * kLog2e;
   if (corr) return launch_prefill_c<true>(q, k, vt, rho, gate, out, B, H, L, d, sl2, s);
   return launch_prefill_c<false>(q, k, vt, rho, gate, out, B, H, L, d, sl2, s);
+}
+
+hipError_t launch_prefill_bf16_train(const void* q, const void* k, const void* vt,
+                                     const void* rho, const float* gate, float* out,
+                                     float* lse, float* rbar, float* corr, int B, int H, int L,
+                                     int d, float scale, hipStream_t s) {
+  const float sl2 = scale * kLog2e;
+  const TrainOut tr{lse, rbar, corr};
+  if (d == 128)
+    return launch_prefill_t<128, PLX_PF_NW_D128, (PLX_PF_PIPE_D128 != 0), true, true>(
+        q, k, vt, rho, gate, out, B, H, L, sl2, s, tr);
+  return launch_prefill_t<64, PLX_PF_NW_D64, (PLX_PF_PIPE_D64 != 0), true, true>(
+      q, k, vt, rho, gate, out, B, H, L, sl2, s, tr);
 }
 
 }  // namespace plx

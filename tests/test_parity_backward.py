@@ -1,0 +1,154 @@
+"""GPU parity of the training forward pass and the backward pass against the
+fp64 CPU oracle (prefill_train, prefill_backward).
+
+Tolerances.  Training statistics: out, rbar and corr within 2e-2 max-abs (the
+bf16 forward's bound); lse within 1e-3 (the partition function sums fp16-rounded
+numerators: relative error <= 2^-11 per term).  Gradients: max-abs error within
+2e-2 x max(1, max|reference|) per tensor.  Gradients scale with the sequence
+length and with dout, so the bound is relative to each tensor's magnitude;
+dout and the softmax-weight gradients are rounded to bf16 for the matrix
+products, which a precision emulation puts at 2e-3 to 4e-3 of that magnitude.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import parallax_oracle as po
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dq", "dk", "dv", "drho")
+
+
+def _plx():
+    import parallax_local_linear_amd as plx
+    return plx
+
+
+def _np(x):
+    return x.detach().cpu().double().numpy()
+
+
+def _dout(shape, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+
+
+def _rel_err(got, ref):
+    return float(np.max(np.abs(got - ref))) / max(1.0, float(np.max(np.abs(ref))))
+
+
+def _run(inp, dout):
+    plx = _plx()
+    out, lse, rbar, corr = plx.prefill_train(inp["q"], inp["k"], inp["v"], inp["rho"],
+                                             inp["gate"])
+    grads = plx.prefill_backward(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"], out,
+                                 corr, lse, rbar, dout)
+    torch.cuda.synchronize()
+    return (out, lse, rbar, corr), grads
+
+
+SHAPES = [(1, 1, 1), (1, 2, 31), (1, 1, 33), (2, 1, 64), (1, 2, 65), (1, 1, 130), (2, 2, 200),
+          (1, 1, 511)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,L", SHAPES)
+def test_train_statistics(B, H, L, d):
+    inp = wl.prefill_inputs(B, H, L, d, "bf16", seed=900 + L + d, device="cuda", rho_std=0.5,
+                            gate=("uniform", 0.2, 1.0))
+    plx = _plx()
+    out, lse, rbar, corr = plx.prefill_train(inp["q"], inp["k"], inp["v"], inp["rho"],
+                                             inp["gate"])
+    plain = plx.prefill(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain)          # the same forward kernel, plus side outputs
+    h = {n: inp[n].cpu() for n in inp}
+    ref = po.prefill_train(h["q"], h["k"], h["v"], h["rho"], h["gate"])
+    errs = {n: float(np.max(np.abs(_np(t) - ref[n])))
+            for n, t in (("out", out), ("lse", lse), ("rbar", rbar), ("corr", corr))}
+    print(f"train B{B} H{H} L{L} d{d}: " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()),
+          flush=True)
+    assert errs["out"] <= 2e-2 and errs["rbar"] <= 2e-2 and errs["corr"] <= 2e-2
+    assert errs["lse"] <= 1e-3
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,L", SHAPES)
+def test_backward_shapes(B, H, L, d):
+    inp = wl.prefill_inputs(B, H, L, d, "bf16", seed=950 + L + d, device="cuda", rho_std=0.5,
+                            gate=("uniform", 0.2, 1.0))
+    dout = _dout((B, H, L, d), 960 + L)
+    _, grads = _run(inp, dout)
+    h = {n: inp[n].cpu() for n in inp}
+    ref = po.prefill_backward(h["q"], h["k"], h["v"], h["rho"], h["gate"], dout.cpu())
+    errs = {n: _rel_err(_np(t), ref[n]) for n, t in zip(GRADS, grads[:4])}
+    errs["dgate"] = _rel_err(_np(grads[4]), ref["dgate"])
+    print(f"backward B{B} H{H} L{L} d{d}: " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()),
+          flush=True)
+    for n, e in errs.items():
+        assert e <= 2e-2, n
+
+
+def test_backward_gate_zero_and_rho_zero():
+    """gate = 0 leaves softmax attention: drho is exactly zero; with rho = 0 the
+    gate gets no gradient.  Both against the oracle as well."""
+    inp = wl.prefill_inputs(1, 2, 150, 128, "bf16", seed=970, device="cuda", rho_std=0.5)
+    dout = _dout((1, 2, 150, 128), 971)
+    inp["gate"].zero_()
+    _, grads = _run(inp, dout)
+    assert float(grads[3].abs().max()) == 0.0
+    h = {n: inp[n].cpu() for n in inp}
+    ref = po.prefill_backward(h["q"], h["k"], h["v"], h["rho"], h["gate"], dout.cpu())
+    for n, t in zip(GRADS, grads[:4]):
+        assert _rel_err(_np(t), ref[n]) <= 2e-2, n
+    inp["gate"].fill_(0.7)
+    inp["rho"].zero_()
+    _, grads = _run(inp, dout)
+    assert float(grads[4].abs().max()) == 0.0
+
+
+def test_backward_deterministic():
+    inp = wl.prefill_inputs(2, 2, 300, 128, "bf16", seed=972, device="cuda", rho_std=0.5)
+    dout = _dout((2, 2, 300, 128), 973)
+    _, a = _run(inp, dout)
+    a = [t.clone() for t in a]
+    _, b = _run(inp, dout)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("wid", [2, 5])
+def test_backward_full_workload_sampled(wid):
+    """The full-size bf16 workloads: every gradient element of sampled heads
+    against the oracle, and the gate gradient of one head (summed over the
+    batch) for workload 2."""
+    w = wl.WORKLOADS[wid]
+    inp = wl.make_workload(wid, device="cuda")
+    dout = _dout((w.B, w.H, w.L, w.d), 980 + wid)
+    _, grads = _run(inp, dout)
+    for t in grads:
+        assert bool(torch.isfinite(t).all())
+    heads = [(0, 0), (w.B - 1, w.H - 1)] if wid == 2 else [(w.B - 1, 5)]
+    if wid == 2:
+        heads += [(b, 0) for b in range(1, w.B)]
+    worst = {n: 0.0 for n in GRADS}
+    dg0 = 0.0
+    for b, hh in heads:
+        x = {n: inp[n][b, hh].double().cpu().numpy() for n in ("q", "k", "v", "rho")}
+        g = float(inp["gate"][hh])
+        ref = po.prefill_head_backward(x["q"], x["k"], x["v"], x["rho"], g, w.scale,
+                                       dout[b, hh].double().cpu().numpy())
+        for n, t, r in zip(GRADS, grads[:4], ref[:4]):
+            worst[n] = max(worst[n], _rel_err(_np(t[b, hh]), r))
+        if hh == 0:
+            dg0 += ref[4]
+        print(f"workload {wid} head ({b},{hh}): " + " ".join(f"{n} {e:.2e}" for n, e in worst.items()),
+              flush=True)
+    for n, e in worst.items():
+        assert e <= 2e-2, n
+    if wid == 2:
+        e = abs(float(grads[4][0]) - dg0) / max(1.0, abs(dg0))
+        print(f"workload 2 dgate[0]: {float(grads[4][0]):.6e} vs {dg0:.6e} (rel {e:.2e})", flush=True)
+        assert e <= 2e-2
