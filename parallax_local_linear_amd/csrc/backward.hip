@@ -15,8 +15,8 @@
 // and C come from the training forward pass.
 //
 // Kernels (one stream, in this order):
-//   bwd_prep_kernel   dO -> bf16 (row-major copy), per-row statistics
-//                     {lse*log2e, rbar, D, F} and per-tile partials of <dO, C>.
+//   bwd_prep_kernel   dO -> bf16 (row-major copy), per-row constants of the
+//                     elementwise step and per-tile partials of <dO, C>.
 //   stage_v_kernel    (bf16 output) transposed 64-row tiles of dO, Q, rho and K
 //                     with the rows of each 32-row group in the order in which a
 //                     lane group of the score MFMAs produces them.
@@ -44,10 +44,10 @@ constexpr int BW_BQ = 32;   // queries per step of the key-stationary kernel
 
 // Launch shapes (waves per workgroup, 16-key blocks per wave), per head dimension.
 #ifndef PLX_BW_KV_NW_D128
-#define PLX_BW_KV_NW_D128 4
+#define PLX_BW_KV_NW_D128 8
 #endif
 #ifndef PLX_BW_KV_KB_D128
-#define PLX_BW_KV_KB_D128 2
+#define PLX_BW_KV_KB_D128 1
 #endif
 #ifndef PLX_BW_KV_NW_D64
 #define PLX_BW_KV_NW_D64 4
@@ -78,7 +78,8 @@ __device__ __forceinline__ int tr_off(int f, int c) {
 }
 
 // ------------------------------------------------------------------- prep
-// Four threads per row, 64 rows per workgroup.
+// 64 rows per workgroup.  Each lane handles 4 consecutive features of a row,
+// so one wave instruction reads 64 / (D/4) whole rows of each fp32 input.
 template <int D>
 __global__ __launch_bounds__(256)
 void bwd_prep_kernel(const float* __restrict__ dout, const float* __restrict__ out,
@@ -86,83 +87,108 @@ void bwd_prep_kernel(const float* __restrict__ dout, const float* __restrict__ o
                      const float* __restrict__ rbar, const float* __restrict__ gate,
                      __bf16* __restrict__ do16, f32x4* __restrict__ stats,
                      float* __restrict__ gpart, int H, int L, int n_t) {
-  constexpr int PER = D / 4;
+  constexpr int LPR = D / 4;                 // lanes per row
+  constexpr int RPW = 64 / LPR;              // rows per wave instruction
+  constexpr int ITER = 16 / RPW;             // 16 rows per wave
   __shared__ float red[4];
   const int bh = blockIdx.x / n_t, t = blockIdx.x % n_t;
   const int h = bh % H;
   const int tid = threadIdx.x;
-  const int row = t * 64 + (tid >> 2);
-  const int part = tid & 3;
-  float fo = 0.f, fc = 0.f, gx = 0.f;
-  if (row < L) {
-    const size_t base = ((size_t)bh * L + row) * D + part * PER;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int sub = lane % LPR;
+  const float g = gate[h];
+  float gsum = 0.f;
+  f32x4 dx[ITER], ox[ITER], cx[ITER];
 #pragma unroll
-    for (int c = 0; c < PER; c += 8) {
-      bf16x8 pk;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const f32x4 dx = *reinterpret_cast<const f32x4*>(dout + base + c + 4 * hf);
-        const f32x4 ox = *reinterpret_cast<const f32x4*>(out + base + c + 4 * hf);
-        const f32x4 cx = *reinterpret_cast<const f32x4*>(corr + base + c + 4 * hf);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const __bf16 b = (__bf16)dx[e];
-          const float dr = (float)b;
-          pk[4 * hf + e] = b;
-          fo = fmaf(dr, ox[e], fo);
-          fc = fmaf(dr, cx[e], fc);
-          gx = fmaf(dx[e], cx[e], gx);
-        }
-      }
-      *reinterpret_cast<bf16x8*>(do16 + base + c) = pk;
+  for (int it = 0; it < ITER; ++it) {
+    const int row = t * 64 + wave * 16 + it * RPW + lane / LPR;
+    if (row < L) {
+      const size_t o = ((size_t)bh * L + row) * D + 4 * sub;
+      dx[it] = *reinterpret_cast<const f32x4*>(dout + o);
+      ox[it] = *reinterpret_cast<const f32x4*>(out + o);
+      cx[it] = *reinterpret_cast<const f32x4*>(corr + o);
+    } else {
+      dx[it] = ox[it] = cx[it] = f32x4{};
     }
   }
-  fo = group_sum<4>(fo);
-  fc = group_sum<4>(fc);
-  gx = group_sum<4>(gx);
-  if (row < L && part == 0) {
-    // D uses o_sa = o + g C; both D and F come from the rounded dO that the
-    // products Delta = dO V^T see, so that the dS rows sum to zero
-    stats[(size_t)bh * L + row] =
-        f32x4{lse[(size_t)bh * L + row] * kLog2e, rbar[(size_t)bh * L + row],
-              fmaf(gate[h], fc, fo), fo};
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int row = t * 64 + wave * 16 + it * RPW + lane / LPR;
+    float fo = 0.f, fc = 0.f, gx = 0.f;
+    __bf16 pk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pk[e] = (__bf16)dx[it][e];
+      const float dr = (float)pk[e];
+      fo = fmaf(dr, ox[it][e], fo);
+      fc = fmaf(dr, cx[it][e], fc);
+      gx = fmaf(dx[it][e], cx[it][e], gx);
+    }
+    fo = group_sum<LPR>(fo);
+    fc = group_sum<LPR>(fc);
+    gx = group_sum<LPR>(gx);
+    if (row < L) {
+      const size_t o = ((size_t)bh * L + row) * D + 4 * sub;
+      uint2 w;
+      w.x = (uint32_t)__builtin_bit_cast(uint16_t, pk[0]) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, pk[1]) << 16);
+      w.y = (uint32_t)__builtin_bit_cast(uint16_t, pk[2]) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, pk[3]) << 16);
+      *reinterpret_cast<uint2*>(do16 + o) = w;
+      if (sub == 0) {
+        // D uses o_sa = o + g C; both D and F come from the rounded dO that the
+        // products Delta = dO V^T see, so that the dS rows sum to zero.  Stored
+        // as the constants of the elementwise step (bwd_elt).
+        const float rb = rbar[(size_t)bh * L + row];
+        const float gD = g * fmaf(g, fc, fo);
+        stats[(size_t)bh * L + row] = f32x4{-lse[(size_t)bh * L + row] * kLog2e,
+                                            fmaf(g, rb, 1.f), gD, -fmaf(gD, rb, fo)};
+        gsum += gx;                          // exact fp32 dO; row order fixed
+      }
+    }
   }
-  // tile partial of sum <dO, C> (exact fp32 dO), lanes then waves in a fixed order
-  float x = (part == 0 && row < L) ? gx : 0.f;
-  x = group_sum<32>(x);
-  x += __shfl_xor(x, 32);
-  if ((tid & 63) == 0) red[tid >> 6] = x;
+  // tile partial of sum <dO, C>: lanes, then waves, in a fixed order
+  gsum = group_sum<32>(gsum);
+  gsum += __shfl_xor(gsum, 32);
+  if (lane == 0) red[wave] = gsum;
   __syncthreads();
   if (tid == 0) gpart[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// dgate[h] = -sum over b and tiles of the partials, one thread per head.
+// dgate[h] = -sum over b and tiles of the partials: one wave per head, each
+// lane a fixed strided subset, then a fixed reduction tree.
 __global__ __launch_bounds__(64)
 void bwd_dgate_kernel(const float* __restrict__ gpart, float* __restrict__ dgate, int B, int H,
                       int n_t) {
-  const int h = blockIdx.x * 64 + threadIdx.x;
-  if (h >= H) return;
+  const int h = blockIdx.x;
+  const int lane = threadIdx.x;
   float s = 0.f;
   for (int b = 0; b < B; ++b)
-    for (int t = 0; t < n_t; ++t) s += gpart[((size_t)b * H + h) * n_t + t];
-  dgate[h] = -s;
+    for (int t = lane; t < n_t; t += 64) s += gpart[((size_t)b * H + h) * n_t + t];
+  s = group_sum<32>(s);
+  s += __shfl_xor(s, 32);
+  if (lane == 0) dgate[h] = -s;
 }
 
-// Elementwise step shared by both main kernels, for one (query, key) score:
-// returns W~ = w (1 - g rc), dS' and dR.
+// Elementwise step shared by both main kernels, for one (query i, key j):
+// score s (the raw <q,k>), r = <rho,k>, dl = <dO,v>, and the row's constants
+//   st = {-lse_i log2e, 1 + g rbar_i, g D_i, -(g D_i rbar_i + F_i)}.
+// Returns W~ = w (1 - g (r - rbar)), dS/scale = w (dl (1 - g (r - rbar)) +
+// g D (r - rbar) - F) and dR = g w (D - dl); the factor `scale` of dS is applied
+// to the accumulated products instead of to every element.
 struct BwdElt {
   float wt, ds, dr;
 };
+template <bool MASK>
 __device__ __forceinline__ BwdElt bwd_elt(bool keep, float s, float r, float dl, f32x4 st,
-                                          float g, float sl2, float scale) {
-  // st = {lse*log2e, rbar, D, F}; a masked score contributes exact zeros
-  const float w = keep ? __builtin_amdgcn_exp2f(fmaf(s, sl2, -st[0])) : 0.f;
-  const float rc = r - st[1];
-  const float t1 = fmaf(-g, rc, 1.f);
+                                          float ng, float sl2) {
+  float w = __builtin_amdgcn_exp2f(fmaf(s, sl2, st[0]));
+  if constexpr (MASK) w = keep ? w : 0.f;      // a masked score contributes exact zeros
+  const float t1 = fmaf(ng, r, st[1]);
   BwdElt e;
   e.wt = w * t1;
-  e.ds = (w * scale) * (fmaf(dl, t1, g * rc * st[2]) - st[3]);
-  e.dr = (g * w) * (st[2] - dl);
+  e.ds = w * fmaf(dl, t1, fmaf(st[2], r, st[3]));
+  e.dr = w * fmaf(ng, dl, st[2]);
   return e;
 }
 
@@ -198,7 +224,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int kw0 = k0 + 16 * KB * wave;
   const size_t head = (size_t)bh * L * D;
   const int n64 = (L + BW_T - 1) / BW_T;
-  const float g = gate[h];
+  const float ng = -gate[h];
+  const float inv_scale = 1.0f / scale;
 
   // B-operand fragments of this wave's keys: key kw0 + 16 kb + c16, features
   // 32 kk + 8 g4 .. +7
@@ -276,7 +303,9 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                         (uint32_t)(16 * lane));
   };
 
-  auto compute = [&](int qs, int buf) {
+  // MASK: the step holds a query before one of this wave's keys, or past L
+  auto compute = [&](int qs, int buf, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
     const uint16_t* st = smem + buf * STAGE;
     const uint16_t* Qs = st;
     const uint16_t* Rs = st + RM;
@@ -311,8 +340,9 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         }
       }
     }
-    // W~, dS', dR in bf16: element e = 4 qb + j of a key's 8 queries, the
-    // position order of the staged transposed tiles
+    // W~, dS/scale, dR/scale in bf16 (dK = scale (Q^T dS/scale + rho^T dR/scale)):
+    // element e = 4 qb + j of a key's 8 queries, the position order of the staged
+    // transposed tiles
     bf16x8 wtp[KB], dsp[KB], drp[KB];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -325,11 +355,11 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         for (int kb = 0; kb < KB; ++kb) {
           const int key = kw0 + 16 * kb + c16;
           const bool keep = qq >= key && qq < L;
-          const BwdElt el = bwd_elt(keep, sa[kb][qb][j], ra[kb][qb][j], da[kb][qb][j], sv, g,
-                                    sl2, scale);
+          const BwdElt el = bwd_elt<MASK>(keep, sa[kb][qb][j], ra[kb][qb][j], da[kb][qb][j], sv,
+                                          ng, sl2);
           wtp[kb][4 * qb + j] = (__bf16)el.wt;
           dsp[kb][4 * qb + j] = (__bf16)el.ds;
-          drp[kb][4 * qb + j] = (__bf16)el.dr;
+          drp[kb][4 * qb + j] = (__bf16)(el.dr * inv_scale);
         }
       }
     }
@@ -360,7 +390,11 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     // the buffer no wave reads again
     load_stage(min(qs + 1, n_qs - 1), 1 - buf);
     // a wave whose keys all follow the step's last query has nothing to add
-    if (qs * BW_BQ + BW_BQ - 1 >= kw0) compute(qs, buf);
+    const int q0 = qs * BW_BQ;
+    if (q0 + BW_BQ - 1 >= kw0) {
+      if (q0 < kw0 + 16 * KB || q0 + BW_BQ > L) compute(qs, buf, std::true_type{});
+      else compute(qs, buf, std::false_type{});
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
@@ -371,7 +405,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     if (key < L) {
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
-        *reinterpret_cast<f32x4*>(dk + head + (size_t)key * D + 16 * fb + 4 * g4) = dk_acc[kb][fb];
+        *reinterpret_cast<f32x4*>(dk + head + (size_t)key * D + 16 * fb + 4 * g4) =
+            dk_acc[kb][fb] * scale;
         *reinterpret_cast<f32x4*>(dv + head + (size_t)key * D + 16 * fb + 4 * g4) = dv_acc[kb][fb];
       }
     }
@@ -409,7 +444,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int qi = qw0 + c16;
   const size_t head = (size_t)bh * L * D;
   const int n64 = (L + BW_T - 1) / BW_T;
-  const float g = gate[h];
+  const float ng = -gate[h];
 
   bf16x8 qf[KSTEPS], rf[KSTEPS], df[KSTEPS];
 #pragma unroll
@@ -502,13 +537,14 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const int kb = 2 * t + hh;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bool keep = !decltype(diag_c)::value || (16 * kb + j <= lim);
-          const BwdElt el = bwd_elt(keep, sa[kb][j], ra[kb][j], da[kb][j], sv, g, sl2, scale);
+          const bool keep = 16 * kb + j <= lim;
+          const BwdElt el = bwd_elt<decltype(diag_c)::value>(keep, sa[kb][j], ra[kb][j], da[kb][j],
+                                                             sv, ng, sl2);
           dsp[4 * hh + j] = (__bf16)el.ds;
           drp[4 * hh + j] = (__bf16)el.dr;
         }
       }
-      // dQ^T += K^T dS'^T,  drho^T += K^T dR^T over the 32 keys of group t
+      // dQ^T += K^T (dS/scale)^T,  drho^T += K^T dR^T over the 32 keys of group t
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(KTs + tr_off<BW_T>(16 * fb + c16, 4 * t + g4));
@@ -535,7 +571,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   if (qi < L) {
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb) {
-      *reinterpret_cast<f32x4*>(dq + head + (size_t)qi * D + 16 * fb + 4 * g4) = dq_acc[fb];
+      *reinterpret_cast<f32x4*>(dq + head + (size_t)qi * D + 16 * fb + 4 * g4) = dq_acc[fb] * scale;
       *reinterpret_cast<f32x4*>(drho + head + (size_t)qi * D + 16 * fb + 4 * g4) = dr_acc[fb];
     }
   }
@@ -639,8 +675,8 @@ hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, 
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dgate_kernel, dim3((unsigned)((H + 63) / 64)), dim3(64), 0, s, gpart,
-                     dgate, B, H, n64);
+  hipLaunchKernelGGL(bwd_dgate_kernel, dim3((unsigned)H), dim3(64), 0, s, gpart, dgate, B, H,
+                     n64);
   return hipGetLastError();
 }
 

@@ -486,12 +486,22 @@ void stage_v_kernel(const __bf16* __restrict__ v, TOUT* __restrict__ vt, int L, 
   const int tid = threadIdx.x;
   const __bf16* src = v + ((size_t)bh * L + (size_t)kt * PF_BC) * D;
   constexpr int CH = PF_BC * D / 8;
-  for (int ch = tid; ch < CH; ch += 256) {
+  constexpr int PER = CH / 256;         // 16-byte chunks per thread
+  // all global loads in flight before the first LDS store
+  u32x4 w[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int ch = tid + 256 * i;
     const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (kt * PF_BC + row < L) w = *reinterpret_cast<const u32x4*>(src + (size_t)row * D + col);
+    w[i] = (kt * PF_BC + row < L) ? *reinterpret_cast<const u32x4*>(src + (size_t)row * D + col)
+                                  : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int ch = tid + 256 * i;
+    const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
     uint32_t* dst = reinterpret_cast<uint32_t*>(tile + row * PITCH + col);
-    dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2]; dst[3] = w[3];
+    dst[0] = w[i][0]; dst[1] = w[i][1]; dst[2] = w[i][2]; dst[3] = w[i][3];
   }
   __syncthreads();
   TOUT* dst = vt + ((size_t)bh * n_kt + kt) * (size_t)(D * PF_BC);
