@@ -13,6 +13,7 @@ from .parallax_oracle import (  # noqa: F401
     prefill_explicit,
     prefill_head,
     prefill_backward,
+    prefill_chunk,
     prefill_head_backward,
     prefill_head_train,
     prefill_rows,

@@ -337,3 +337,39 @@ def prefill_backward(q, k, v, rho, gate, dout, scale=None, heads=None):
         res["dq"][b, h], res["dk"][b, h], res["dv"][b, h], res["drho"][b, h] = g[:4]
         res["dgate"][h] += g[4]
     return res
+
+
+# ---------------------------------------------------------- chunked prefill
+# The step between prefill and decode (section "Contributions": the kernels are
+# meant for any batch size and context length): each sequence b already holds
+# ctx[b] keys in its cache and appends a chunk of n_b new queries, whose keys and
+# values have been written to cache positions ctx[b] .. ctx[b]+n_b-1.  Chunk
+# query j sits at position p = ctx[b] + j and attends cache positions 0..p
+# (causal), so every output row is one decode query (Eq. 2) over the cache
+# prefix it sees.  Queries come packed and token-major: sequence b owns rows
+# cu_q[b] .. cu_q[b+1]-1 of q, rho and out ([T, H, d]).
+
+def prefill_chunk(q, kcache, vcache, rho, gate, cu_q, ctx, scale=None, rows=None):
+    """Chunked causal prefill against a KV cache.  q, rho [T,H,d_k];
+    kcache [B,H,Lmax,d_k]; vcache [B,H,Lmax,d_v]; cu_q [B+1]; ctx [B]; gate [H].
+    Returns out [T,H,d_v].  `rows` optionally restricts the work to a list of
+    token rows (the others stay NaN)."""
+    B, H, Lmax, dk = kcache.shape
+    dv = vcache.shape[-1]
+    sc = _default_scale(dk, scale)
+    qf, rf, gf = _f64(q), _f64(rho), _f64(gate)
+    cu = [int(x) for x in _f64(cu_q)]
+    cx = [int(x) for x in _f64(ctx)]
+    T = qf.shape[0]
+    out = np.full((T, H, dv), np.nan)
+    want = None if rows is None else set(int(r) for r in rows)
+    for b in range(B):
+        for j, t in enumerate(range(cu[b], cu[b + 1])):
+            if want is not None and t not in want:
+                continue
+            p = cx[b] + j
+            for h in range(H):
+                K = _f64(kcache[b, h, : p + 1])
+                V = _f64(vcache[b, h, : p + 1])
+                out[t, h] = decode_stream(qf[t, h], K, V, rf[t, h], gf[h], sc)
+    return out
