@@ -20,6 +20,9 @@ decode and the d=64 prefill) are timed too and reported under "extra".
 the gradient needs) and the backward pass on the prefill workloads; its
 TFLOP/s count 16*d flops per causal pair (S and R recomputed, dO V^T, and the
 dV, dK (two), dQ and drho products), twice the forward's 8*d.
+"chunk" times the chunked prefill against a KV cache on two shapes: long
+chunks on a 4096-key context (TFLOP/s) and 16-query chunks on an 8192-key
+context (HBM GB/s of the cache rows read).
 "softmax_relative" times the same kernels with the correction branch compiled
 out (plain causal softmax attention) against the Parallax kernels on each
 workload, alternating the two launch by launch, and reports the time ratio.
@@ -170,6 +173,7 @@ def main():
                     help="skip the timing against the softmax-only kernels")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the training forward and backward timing")
+    ap.add_argument("--no-chunk", action="store_true", help="skip the chunked prefill timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size kernel for scaling HBM byte counters)")
@@ -280,6 +284,8 @@ def main():
         res["calib_copy_bytes"] = {"read": n * 4, "write": n * 4}
         del src, dst
 
+    if not args.no_chunk:
+        res["chunk"] = [chunk_block(torch, plx, wl, name, dev) for name in sorted(wl.CHUNK_WORKLOADS)]
     if not args.no_backward:
         log("backward: workload 2")
         res["backward"] = [backward_block(torch, plx, wl, pin, wp)]
@@ -303,6 +309,35 @@ def main():
         res["cpu_baseline"] = cpu_baseline_prefill(pin, wp)
         res["decode"]["cpu_baseline"] = cpu_baseline_decode(din, wd)
     print(json.dumps(res), flush=True)
+
+
+def chunk_block(torch, plx, wl, name, dev, steps=10):
+    """Chunked prefill (V^T staging of the rows read + fused kernel) on one
+    chunk workload, workspace allocated before timing."""
+    log(f"chunk: {name}")
+    cw = wl.CHUNK_WORKLOADS[name]
+    inp = wl.make_chunk_workload(name, device=dev)
+    B, H, d = cw["B"], cw["H"], cw["d"]
+    Lmax = inp["kcache"].shape[2]
+    ws = torch.empty(int(plx.lib().parallax_prefill_chunk_workspace_bytes(B, H, Lmax, d)),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((inp["T"], H, d), dtype=torch.float32, device=dev)
+    tm = Timer(torch)
+    for _ in range(steps + 2):
+        tm.run("chunk", lambda: plx.prefill_chunk(inp["q"], inp["kcache"], inp["vcache"],
+                                                  inp["rho"], inp["gate"], inp["cu_q"],
+                                                  inp["ctx"], inp["max_q"], out=out,
+                                                  workspace=ws))
+    torch.cuda.synchronize()
+    ms = tm.ms("chunk", 2)
+    ctx, n = [cw["ctx"]] * B, [cw["n"]] * B
+    fl = wl.chunk_flops(ctx, n, H, d)
+    nb = wl.chunk_bytes(ctx, n, H, d)
+    res = {"workload": name, "ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 2),
+           "GB/s": round(nb / ms / 1e6, 1), "flops": fl, "bytes": nb}
+    del inp, ws, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def backward_block(torch, plx, wl, inp, w, steps=10):

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 3
+#define PARALLAX_ABI_VERSION 4
 
 typedef enum {
   PLX_OK = 0,
@@ -147,6 +147,35 @@ int parallax_decode_combine(const float* partials, const float* gate, const int3
 
 /* The split size parallax_decode uses when split_keys is 0. */
 int parallax_decode_default_split(int B, int H, int Lmax, int d);
+
+/* ----------------------------------------------------------- chunked prefill
+ * The step between prefill and decode (the pages' kernels target every batch
+ * size and context length, section "Contributions"): sequence b holds ctx[b]
+ * keys in its cache and appends a chunk of n_b = cu_q[b+1] - cu_q[b] queries,
+ * whose keys and values the caller has already written to cache positions
+ * ctx[b] .. ctx[b]+n_b-1.  Chunk query j sits at position ctx[b] + j and
+ * attends cache positions 0 .. ctx[b] + j (Eq. 2 over that prefix).
+ *   q, rho  : [T, H, d] bf16, packed and token-major: sequence b owns rows
+ *             cu_q[b] .. cu_q[b+1]-1
+ *   kcache, vcache : [B, H, Lmax, d] bf16
+ *   gate    : [H] fp32
+ *   cu_q    : [B+1] int32 device, non-decreasing row offsets into q
+ *   ctx     : [B] int32 device, cached keys before each chunk
+ *   out     : [T, H, d] fp32; rows of the chunks are written, others untouched
+ * max_q must be at least the largest n_b (it sizes the grid).  The device
+ * clamps cu_q to [0, T], n_b to min(max_q, Lmax) and ctx[b] to
+ * [0, Lmax - n_b], so no access leaves q or the cache.  Cache rows at or past
+ * ctx[b] + n_b are never read.  PLX_BF16 only.  The workspace (at least
+ * parallax_prefill_chunk_workspace_bytes(B, H, Lmax, d) bytes, or NULL to let
+ * the library allocate on `stream`) holds the fp16 V^T tiles of the cache
+ * rows the chunks read. */
+size_t parallax_prefill_chunk_workspace_bytes(int B, int H, int Lmax, int d);
+
+int parallax_prefill_chunk(const void* q, const void* kcache, const void* vcache,
+                           const void* rho, const float* gate, float* out,
+                           const int32_t* cu_q, const int32_t* ctx, int B, int H, int T,
+                           int Lmax, int max_q, int d, float scale, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* --------------------------------------------------------- softmax baseline
  * Plain causal softmax attention, o_i = o^SA_i (Eq. 2 without the correction

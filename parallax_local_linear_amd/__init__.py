@@ -27,7 +27,7 @@ __all__ = ["prefill", "decode", "prefill_stage_v", "prefill_attend", "decode_par
            "decode_combine", "prefill_workspace_bytes", "decode_workspace_bytes",
            "decode_default_split", "softmax_prefill", "softmax_prefill_attend",
            "softmax_decode", "prefill_train", "prefill_backward",
-           "prefill_backward_workspace_bytes", "ParallaxError"]
+           "prefill_backward_workspace_bytes", "prefill_chunk", "ParallaxError"]
 
 _DT = {torch.bfloat16: PLX_BF16, torch.float32: PLX_F32}
 
@@ -186,6 +186,38 @@ def prefill_backward(q, k, v, rho, gate, out, corr, lse, rbar, dout, scale=None,
             *(_ptr(t) for t in grads), B, H, L, d, _scale(scale, d), PLX_BF16,
             _ptr(workspace), wsb)
     return grads
+
+
+def prefill_chunk(q, kcache, vcache, rho, gate, cu_q, ctx, max_q, scale=None, out=None,
+                  workspace=None):
+    """Chunked causal prefill against a KV cache (bf16).  q, rho: [T, H, d]
+    packed token-major; kcache, vcache: [B, H, Lmax, d] holding each chunk's
+    own keys at positions ctx[b] .. ctx[b]+n_b-1; cu_q [B+1] and ctx [B] int32 on
+    the GPU; max_q >= the largest chunk.  Returns out [T, H, d] fp32."""
+    _check("q", q, torch.bfloat16)
+    _check("kcache", kcache, torch.bfloat16)
+    if q.dim() != 3 or kcache.dim() != 4:
+        raise ValueError("q must be [T, H, d] and kcache [B, H, Lmax, d]")
+    T, H, d = q.shape
+    B, _, Lmax, _ = kcache.shape
+    _check("kcache", kcache, torch.bfloat16, (B, H, Lmax, d), q.device)
+    _check("vcache", vcache, torch.bfloat16, (B, H, Lmax, d), q.device)
+    _check("rho", rho, torch.bfloat16, (T, H, d), q.device)
+    _check("gate", gate, torch.float32, (H,), q.device)
+    _check("cu_q", cu_q, torch.int32, (B + 1,), q.device)
+    _check("ctx", ctx, torch.int32, (B,), q.device)
+    if out is None:
+        out = torch.empty((T, H, d), dtype=torch.float32, device=q.device)
+    _check("out", out, torch.float32, (T, H, d), q.device)
+    wsb = int(lib().parallax_prefill_chunk_workspace_bytes(B, H, Lmax, d))
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+    _check("workspace", workspace, device=q.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _launch(q.device, "parallax_prefill_chunk", _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(rho),
+            _ptr(gate), _ptr(out), _ptr(cu_q), _ptr(ctx), B, H, T, Lmax, int(max_q), d,
+            _scale(scale, d), PLX_BF16, _ptr(workspace), wsb)
+    return out
 
 
 def prefill_stage_v(v, vt=None):

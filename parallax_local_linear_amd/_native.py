@@ -42,6 +42,8 @@ SIGNATURES = {
     "parallax_prefill_train": (_i, [_vp] * 9 + [_i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "parallax_prefill_backward_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "parallax_prefill_backward": (_i, [_vp] * 15 + [_i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "parallax_prefill_chunk_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "parallax_prefill_chunk": (_i, [_vp] * 8 + [_i] * 6 + [_f, _i, _vp, _sz, _vp]),
 }
 
 _lib = None

@@ -36,6 +36,10 @@ hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, 
                                    int B, int H, int L, int d, float scale, void* ws,
                                    hipStream_t s);
 size_t bwd_workspace_bytes(int B, int H, int L, int d);
+hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, const void* rho,
+                                const float* gate, float* out, const int* cu_q, const int* ctx,
+                                int B, int H, int T, int Lmax, int max_q, int d, float scale,
+                                void* vt, hipStream_t s);
 }  // namespace plx
 
 namespace {
@@ -389,6 +393,38 @@ int parallax_prefill_backward(const void* q, const void* k, const void* v, const
                                               dk, dv, drho, dgate, B, H, L, d,
                                               eff_scale(scale, d), ws, s);
   if (e != hipSuccess) return launch_fail(fn, "backward", e);
+  return ok();
+}
+
+size_t parallax_prefill_chunk_workspace_bytes(int B, int H, int Lmax, int d) {
+  if (B <= 0 || H <= 0 || Lmax <= 0 || (d != 64 && d != 128)) return 0;
+  return vt_bytes(B, H, Lmax, d);
+}
+
+int parallax_prefill_chunk(const void* q, const void* kcache, const void* vcache, const void* rho,
+                           const float* gate, float* out, const int32_t* cu_q,
+                           const int32_t* ctx, int B, int H, int T, int Lmax, int max_q, int d,
+                           float scale, int dtype, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  const char* fn = "parallax_prefill_chunk";
+  int st = PLX_OK;
+  if (!dims_ok(B, H, Lmax, d, fn, "Lmax", &st)) return st;
+  if (!dtype_ok(dtype, fn, &st)) return st;
+  if (dtype != PLX_BF16) return fail(PLX_EUNSUPPORTED, "%s: only PLX_BF16 is supported", fn);
+  if (T <= 0 || max_q <= 0)
+    return fail(PLX_EINVAL, "%s: T and max_q must be positive (got %d, %d)", fn, T, max_q);
+  if ((long long)T * H * d > kMaxElems) return fail(PLX_EINVAL, "%s: tensor too large", fn);
+  if (!q || !kcache || !vcache || !rho || !gate || !out || !cu_q || !ctx)
+    return fail(PLX_EINVAL, "%s: null pointer", fn);
+  hipStream_t s = (hipStream_t)stream;
+  Scratch scratch;
+  void* ws = nullptr;
+  if (!get_workspace(workspace, workspace_bytes, vt_bytes(B, H, Lmax, d), s, &scratch, &ws, fn,
+                     &st))
+    return st;
+  hipError_t e = plx::launch_prefill_chunk(q, kcache, vcache, rho, gate, out, cu_q, ctx, B, H, T,
+                                           Lmax, max_q, d, eff_scale(scale, d), ws, s);
+  if (e != hipSuccess) return launch_fail(fn, "chunk", e);
   return ok();
 }
 

@@ -121,14 +121,39 @@ __host__ __device__ constexpr int vt_key_of_pos(int p) {
   return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
 }
 
+// Chunked prefill against a KV cache: sequence b owns token rows
+// cu_q[b] .. cu_q[b+1]-1 of q, rho and out ([T, H, D], token-major) and puts
+// them at cache positions ctx[b] + j; its keys are cache rows 0 .. ctx[b]+n_b-1
+// of K [B, H, Lmax, D] and of the staged V^T.  The device clamps every length so
+// that no access leaves q (T rows) or the cache (Lmax rows).
+struct ChunkArgs {
+  const int* cu_q;
+  const int* ctx;
+  int T;        // rows of q, rho and out
+  int Lmax;     // cache rows per (b, h)
+  int max_q;    // largest chunk: the grid covers ceil(max_q / queries per workgroup)
+  int n64max;   // staged V^T tiles per (b, h): ceil(Lmax / 64)
+};
+// (first row, queries, position of query 0) of sequence b, clamped
+__device__ __forceinline__ void chunk_geometry(const ChunkArgs& ca, int b, int* c0, int* n_q,
+                                               int* pos0) {
+  const int a = min(max(ca.cu_q[b], 0), ca.T);
+  const int e = min(max(ca.cu_q[b + 1], a), ca.T);
+  *c0 = a;
+  *n_q = min(e - a, min(ca.max_q, ca.Lmax));
+  *pos0 = min(max(ca.ctx[b], 0), ca.Lmax - *n_q);
+}
+
 // Second launch bound: at least two waves per SIMD, which caps the register
 // budget at 256 per lane and keeps every MFMA operand in VGPRs.
 // CORR = false compiles the covariance branch out (no R, T, A_r or c): plain
 // causal softmax attention through the same staging, tiling and schedule, the
 // baseline for the cost of the correction.  SAVE = true (training) also writes
 // what the backward pass needs: the natural-log partition function of every
-// row, rbar = c / l and the correction vector (u - o_sa rbar).
-template <int D, int NW, bool PIPE, bool CORR, bool SAVE>
+// row, rbar = c / l and the correction vector (u - o_sa rbar).  VARLEN = true
+// is the chunked prefill (ChunkArgs): the same tile loop with the causal mask
+// offset by the chunk's cache position.
+template <int D, int NW, bool PIPE, bool CORR, bool SAVE, bool VARLEN>
 __global__ __launch_bounds__(64 * NW, CORR ? (D == 64 ? PLX_PF_MINW_D64 : PLX_PF_MINW_D128)
                                           : (D == 64 ? PLX_SM_MINW_D64 : PLX_SM_MINW_D128))
 void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -136,8 +161,9 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
                          const float* __restrict__ gate, float* __restrict__ out,
                          float* __restrict__ lse_out, float* __restrict__ rbar_out,
                          float* __restrict__ corr_out, int H, int L, int BH, int n_qt,
-                         float sl2) {
+                         float sl2, ChunkArgs ca) {
   static_assert(CORR || !SAVE, "the training statistics belong to the Parallax kernel");
+  static_assert(!(SAVE && VARLEN), "the training statistics are for whole sequences");
   using LY = PfLayout<D>;
   constexpr int PF_BR = 16 * NW;                         // queries per workgroup
   constexpr int PF_THREADS = 64 * NW;
@@ -161,11 +187,29 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   const size_t head = (size_t)bh * L * D;
   const int n_kt_all = (L + PF_BC - 1) / PF_BC;
 
+  // Geometry of this head.  Prefill: L queries at positions 0 .. L-1 against
+  // the same L keys.  Chunk: n_q queries at positions pos0 + j against the first
+  // pos0 + n_q cache keys, rows token-major (stride H*D).
+  int n_q = L, pos0 = 0;
+  size_t qbase = head, qstride = D;
+  const __bf16* kh = k + head;
+  const _Float16* vth = vt + (size_t)bh * n_kt_all * (D * PF_BC);
+  if constexpr (VARLEN) {
+    int c0;
+    chunk_geometry(ca, bh / H, &c0, &n_q, &pos0);
+    if (q0 >= n_q) return;                       // uniform over the workgroup
+    qbase = ((size_t)c0 * H + h) * D;
+    qstride = (size_t)H * D;
+    kh = k + (size_t)bh * ca.Lmax * D;
+    vth = vt + (size_t)bh * ca.n64max * (D * PF_BC);
+  }
+  const int n_k = pos0 + n_q;
+
   // B-operand fragments: query qi, features 32*kk + 8*g4 .. +7
   bf16x8 qf[KSTEPS], rf[KSTEPS];
-  if (qi < L) {
-    const bf16x8* qp = reinterpret_cast<const bf16x8*>(q + head + (size_t)qi * D);
-    const bf16x8* rp = CORR ? reinterpret_cast<const bf16x8*>(rho + head + (size_t)qi * D)
+  if (qi < n_q) {
+    const bf16x8* qp = reinterpret_cast<const bf16x8*>(q + qbase + (size_t)qi * qstride);
+    const bf16x8* rp = CORR ? reinterpret_cast<const bf16x8*>(rho + qbase + (size_t)qi * qstride)
                             : nullptr;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
@@ -196,9 +240,9 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones8[e] = (_Float16)1.0f;
 
-  const int last_q = min(q0 + PF_BR, L) - 1;
-  const int n_kt = last_q / PF_BC + 1;
-  const int wave_last_q = min(qw0 + 15, L - 1);
+  const int last_pos = pos0 + min(q0 + PF_BR, n_q) - 1;
+  const int n_kt = last_pos / PF_BC + 1;
+  const int wave_last_pos = pos0 + min(qw0 + 15, n_q - 1);
 
   // Tiles move HBM -> LDS with buffer_load_dwordx4 ... lds: each lane's 16
   // bytes land at (wave-uniform base) + 16 * lane, so one wave instruction
@@ -226,17 +270,17 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     const int r = e / PF_BC, pc = (e % PF_BC) / 8;
     voff[i] = (uint32_t)((r * PF_BC + ((pc ^ (r & 7)) << 3)) * 2);
   }
-  const char* kbase = reinterpret_cast<const char*>(k + head);
+  const char* kbase = reinterpret_cast<const char*>(kh);
   // blocks [i0, i1) of this wave's share of a K tile
   auto load_k = [&](int kt, int buf, auto i0, auto i1) {
-    const int rows = min(PF_BC, L - kt * PF_BC);
+    const int rows = min(PF_BC, n_k - kt * PF_BC);
     const char* tile = kbase + (size_t)kt * PF_BC * D * 2;
 #pragma unroll
     for (int i = decltype(i0)::value; i < decltype(i1)::value; ++i)
       buffer_load_lds16(tile, rows * D * 2, smem + buf * LY::K_ELEMS + (i * NW + wave_u) * 512,
                         koff[i]);
   };
-  const char* vbase = reinterpret_cast<const char*>(vt + (size_t)bh * n_kt_all * (D * PF_BC));
+  const char* vbase = reinterpret_cast<const char*>(vth);
   auto load_v = [&](int kt, int buf) {
     const char* tile = vbase + (size_t)kt * (D * PF_BC) * 2;
 #pragma unroll
@@ -268,8 +312,11 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     }
   };
 
-  // tiles this wave computes: 0 .. n_w-1 (a row always sees key 0 of tile 0)
-  const int n_w = (qw0 < L) ? wave_last_q / PF_BC + 1 : 0;
+  // tiles this wave computes: 0 .. n_w-1 (a row always sees key 0 of tile 0);
+  // a tile needs the causal mask when its last key follows the wave's first
+  // query (for a whole-sequence prefill, only the wave's last tile)
+  const int n_w = (qw0 < n_q) ? wave_last_pos / PF_BC + 1 : 0;
+  auto needs_mask = [&](int t) { return t * PF_BC + PF_BC - 1 > pos0 + qw0; };
 
   // K and V tiles are double-buffered.  Pipelined schedule: K runs one tile
   // ahead of V; in iteration kt the waves read K of tile kt+1 and V of tile kt
@@ -291,7 +338,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // row max of one tile's scores; the four lanes that share a query combine.
   auto tile_max = [&](f32x4 (&sa)[4], int kt_, auto diag_c) -> float {
     if constexpr (decltype(diag_c)::value) {
-      const int lim = qi - kt_ * PF_BC - 4 * g4;   // key offset 16*kb + j is kept iff <= lim
+      const int lim = pos0 + qi - kt_ * PF_BC - 4 * g4;   // key offset 16*kb + j kept iff <= lim
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
@@ -380,7 +427,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   if constexpr (PIPE) {
     if (n_w > 0) {
       scores(std::integral_constant<int, 0>{}, sc, rc);
-      m_run = (n_w == 1) ? tile_max(sc, 0, std::true_type{}) : tile_max(sc, 0, std::false_type{});
+      m_run = needs_mask(0) ? tile_max(sc, 0, std::true_type{}) : tile_max(sc, 0, std::false_type{});
     }
     // iteration 0 overwrites K buffer 0: every wave must be done reading it
     __syncthreads();
@@ -404,16 +451,16 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       if constexpr (PIPE) {
         if (kt + 1 < n_w) {
           const float m_next =
-              (kt + 2 == n_w) ? pipe_step(kt, par, std::true_type{}, cs, cr, ns, nr)
-                              : pipe_step(kt, par, std::false_type{}, cs, cr, ns, nr);
+              needs_mask(kt + 1) ? pipe_step(kt, par, std::true_type{}, cs, cr, ns, nr)
+                                 : pipe_step(kt, par, std::false_type{}, cs, cr, ns, nr);
           rescale_to(m_next);
         } else {
           softmax_pv(par, cs, cr);
         }
       } else {
         scores(par, cs, cr);
-        const float m_tile = (kt + 1 == n_w) ? tile_max(cs, kt, std::true_type{})
-                                             : tile_max(cs, kt, std::false_type{});
+        const float m_tile = needs_mask(kt) ? tile_max(cs, kt, std::true_type{})
+                                            : tile_max(cs, kt, std::false_type{});
         if (kt == 0) m_run = m_tile;            // accumulators are still zero
         rescale_to(m_tile);
         softmax_pv(par, cs, cr);
@@ -430,11 +477,11 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // epilogue: o = o_sa - g (u - o_sa * rbar), o_sa = O/l, u = A_r/l, rbar = c/l
   const float l_tot = acc_l[0];
   const float c_tot = acc_c[0];
-  if (qi < L) {
+  if (qi < n_q) {
     const float inv = 1.0f / l_tot;
     const float rbar = c_tot * inv;
     const float gh = CORR ? gate[h] : 0.f;
-    float* orow = out + head + (size_t)qi * D;
+    float* orow = out + qbase + (size_t)qi * qstride;
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb) {
       f32x4 o;
@@ -475,15 +522,25 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 // the rows of each 32-row group in vt_key_of_pos order.
 // One workgroup per (head, 64-row tile): coalesced 16-B loads into LDS, then
 // each thread gathers 8 rows of one feature, converts and stores 16 B.
-template <int D, typename TOUT>
+// VARLEN: v is the cache [B, H, L = Lmax, D]; only the tiles holding keys
+// 0 .. ctx[b] + n_b - 1 of each head are written (the ones the chunk reads).
+template <int D, typename TOUT, bool VARLEN = false>
 __global__ __launch_bounds__(256)
-void stage_v_kernel(const __bf16* __restrict__ v, TOUT* __restrict__ vt, int L, int n_kt) {
+void stage_v_kernel(const __bf16* __restrict__ v, TOUT* __restrict__ vt, int L, int n_kt,
+                    ChunkArgs ca = {}, int H = 1) {
   typedef TOUT outx8 __attribute__((ext_vector_type(8)));
   constexpr int PITCH = D + 2;     // odd dword pitch spreads the column reads over banks
   __shared__ uint16_t tile[PF_BC * PITCH];
   const int bh = blockIdx.x / n_kt;
   const int kt = blockIdx.x % n_kt;
   const int tid = threadIdx.x;
+  int n_valid = L;                      // rows of this head that exist
+  if constexpr (VARLEN) {
+    int c0, n_q, pos0;
+    chunk_geometry(ca, bh / H, &c0, &n_q, &pos0);
+    n_valid = pos0 + n_q;
+    if (kt * PF_BC >= n_valid) return;  // uniform over the workgroup
+  }
   const __bf16* src = v + ((size_t)bh * L + (size_t)kt * PF_BC) * D;
   constexpr int CH = PF_BC * D / 8;
   constexpr int PER = CH / 256;         // 16-byte chunks per thread
@@ -493,8 +550,9 @@ void stage_v_kernel(const __bf16* __restrict__ v, TOUT* __restrict__ vt, int L, 
   for (int i = 0; i < PER; ++i) {
     const int ch = tid + 256 * i;
     const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-    w[i] = (kt * PF_BC + row < L) ? *reinterpret_cast<const u32x4*>(src + (size_t)row * D + col)
-                                  : u32x4{0u, 0u, 0u, 0u};
+    w[i] = (kt * PF_BC + row < n_valid)
+               ? *reinterpret_cast<const u32x4*>(src + (size_t)row * D + col)
+               : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -546,16 +604,17 @@ struct TrainOut {
   float* corr;
 };
 
-template <int D, int NW, bool PIPE, bool CORR, bool SAVE = false>
+template <int D, int NW, bool PIPE, bool CORR, bool SAVE = false, bool VARLEN = false>
 static hipError_t launch_prefill_t(const void* q, const void* k, const void* vt,
                                    const void* rho, const float* gate, float* out, int B,
-                                   int H, int L, float sl2, hipStream_t s, TrainOut tr = {}) {
+                                   int H, int L, float sl2, hipStream_t s, TrainOut tr = {},
+                                   ChunkArgs ca = {}) {
   const int BH = B * H;
-  const int n_qt = (L + 16 * NW - 1) / (16 * NW);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, PIPE, CORR, SAVE>), dim3((unsigned)(BH * n_qt)),
-                     dim3(64 * NW), 0, s, (const __bf16*)q, (const __bf16*)k,
-                     (const _Float16*)vt, (const __bf16*)rho, gate, out, tr.lse, tr.rbar,
-                     tr.corr, H, L, BH, n_qt, sl2);
+  const int n_qt = ((VARLEN ? ca.max_q : L) + 16 * NW - 1) / (16 * NW);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, PIPE, CORR, SAVE, VARLEN>),
+                     dim3((unsigned)(BH * n_qt)), dim3(64 * NW), 0, s, (const __bf16*)q,
+                     (const __bf16*)k, (const _Float16*)vt, (const __bf16*)rho, gate, out, tr.lse,
+                     tr.rbar, tr.corr, H, L, BH, n_qt, sl2, ca);
   return hipGetLastError();
 }
 
@@ -578,6 +637,30 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* vt, con
   const float sl2 = scale * kLog2e;
   if (corr) return launch_prefill_c<true>(q, k, vt, rho, gate, out, B, H, L, d, sl2, s);
   return launch_prefill_c<false>(q, k, vt, rho, gate, out, B, H, L, d, sl2, s);
+}
+
+// Chunked prefill: stage V^T of the cache rows each chunk reads, then attend.
+hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, const void* rho,
+                                const float* gate, float* out, const int* cu_q, const int* ctx,
+                                int B, int H, int T, int Lmax, int max_q, int d, float scale,
+                                void* vt, hipStream_t s) {
+  const float sl2 = scale * kLog2e;
+  const int n64 = (Lmax + PF_BC - 1) / PF_BC;
+  const ChunkArgs ca{cu_q, ctx, T, Lmax, max_q, n64};
+  const dim3 grid((unsigned)(B * H * n64));
+  if (d == 128)
+    hipLaunchKernelGGL((stage_v_kernel<128, _Float16, true>), grid, dim3(256), 0, s,
+                       (const __bf16*)vc, (_Float16*)vt, Lmax, n64, ca, H);
+  else
+    hipLaunchKernelGGL((stage_v_kernel<64, _Float16, true>), grid, dim3(256), 0, s,
+                       (const __bf16*)vc, (_Float16*)vt, Lmax, n64, ca, H);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (d == 128)
+    return launch_prefill_t<128, PLX_PF_NW_D128, (PLX_PF_PIPE_D128 != 0), true, false, true>(
+        q, kc, vt, rho, gate, out, B, H, Lmax, sl2, s, {}, ca);
+  return launch_prefill_t<64, PLX_PF_NW_D64, (PLX_PF_PIPE_D64 != 0), true, false, true>(
+      q, kc, vt, rho, gate, out, B, H, Lmax, sl2, s, {}, ca);
 }
 
 hipError_t launch_prefill_bf16_train(const void* q, const void* k, const void* vt,

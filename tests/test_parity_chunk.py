@@ -1,0 +1,119 @@
+"""GPU parity of the chunked prefill against a KV cache (parallax_prefill_chunk)
+with the fp64 CPU oracle (prefill_chunk).  Tolerance: 2e-2 max-abs, the bf16
+forward's bound."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import parallax_oracle as po
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _plx():
+    import parallax_local_linear_amd as plx
+    return plx
+
+
+def _run(inp, out=None):
+    out = _plx().prefill_chunk(inp["q"], inp["kcache"], inp["vcache"], inp["rho"], inp["gate"],
+                               inp["cu_q"], inp["ctx"], inp["max_q"], out=out)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle(inp, rows=None):
+    h = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in inp.items()}
+    return po.prefill_chunk(h["q"], h["kcache"], h["vcache"], h["rho"], h["gate"], h["cu_q"],
+                            h["ctx"], rows=rows)
+
+
+CASES = [  # (ctx per sequence, chunk length per sequence)
+    ([0], [1]),
+    ([0], [65]),
+    ([1], [1]),
+    ([63, 64, 65], [1, 2, 3]),
+    ([60, 4, 0, 130], [16, 17, 15, 64]),
+    ([1000, 7], [65, 200]),
+    ([100, 0, 33, 257, 5], [33, 1, 128, 9, 300]),
+]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "ctx" + "-".join(map(str, c[0])) + "_n" +
+                         "-".join(map(str, c[1])))
+def test_chunk_cases(case, d):
+    ctx, n = case
+    inp = wl.chunk_inputs(3, d, ctx, n, seed=1200 + sum(ctx) + sum(n) + d, device="cuda",
+                          rho_std=0.5)
+    out = _run(inp).cpu().double().numpy()
+    ref = _oracle(inp)
+    err = float(np.max(np.abs(out - ref)))
+    print(f"chunk d{d} ctx{ctx} n{n}: max-abs {err:.3e}", flush=True)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_empty_cache_chunk_is_the_prefill(d):
+    """ctx = 0 and one sequence: bit-identical to the whole-sequence prefill
+    (the same kernel arithmetic over the same tiles)."""
+    plx = _plx()
+    L, H = 333, 2
+    inp = wl.chunk_inputs(H, d, [0], [L], seed=1300 + d, device="cuda", rho_std=0.5)
+    out = _run(inp)
+    q = inp["q"].transpose(0, 1).unsqueeze(0).contiguous()
+    rho = inp["rho"].transpose(0, 1).unsqueeze(0).contiguous()
+    ref = plx.prefill(q, inp["kcache"], inp["vcache"], rho, inp["gate"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref[0].transpose(0, 1))
+
+
+def test_cache_past_the_chunk_is_never_read_and_other_rows_untouched():
+    ctx, n = [50, 200, 3], [20, 70, 100]
+    inp = wl.chunk_inputs(2, 128, ctx, n, seed=1310, device="cuda", Lmax=400)
+    a = _run(inp).clone()
+    for b in range(3):
+        inp["kcache"][b, :, ctx[b] + n[b]:] = float("nan")
+        inp["vcache"][b, :, ctx[b] + n[b]:] = float("nan")
+    # an out buffer with 5 extra rows past the packed chunks, filled with a sentinel
+    T = sum(n)
+    out = torch.full((T + 5, 2, 128), -7.0, dtype=torch.float32, device="cuda")
+    _plx().prefill_chunk(inp["q"], inp["kcache"], inp["vcache"], inp["rho"], inp["gate"],
+                         inp["cu_q"], inp["ctx"], inp["max_q"], out=out[:T])
+    torch.cuda.synchronize()
+    assert torch.equal(out[:T], a)
+    assert bool((out[T:] == -7.0).all())
+
+
+def test_bad_lengths_are_clamped_on_the_device():
+    """ctx beyond the cache and cu_q beyond T are clamped, not followed: the
+    call stays in bounds and the well-formed sequences are unaffected."""
+    inp = wl.chunk_inputs(2, 64, [10, 20], [5, 6], seed=1320, device="cuda", Lmax=40)
+    good = _run(inp).clone()
+    bad = dict(inp)
+    bad["ctx"] = torch.tensor([10, 10 ** 6], dtype=torch.int32, device="cuda")
+    out = _run(bad)
+    assert torch.equal(out[:5], good[:5])
+    assert bool(torch.isfinite(out).all())
+
+
+@pytest.mark.parametrize("name", sorted(wl.CHUNK_WORKLOADS))
+def test_chunk_workload_sampled(name):
+    """The benchmark's chunked workloads: sampled token rows of every sequence
+    against the oracle."""
+    inp = wl.make_chunk_workload(name, device="cuda")
+    out = _run(inp)
+    assert bool(torch.isfinite(out).all())
+    cu = inp["cu_q"].tolist()
+    rng = np.random.default_rng(7)
+    rows = []
+    for b in range(0, len(cu) - 1, max(1, (len(cu) - 1) // 4)):
+        rows += [cu[b], cu[b + 1] - 1] + [int(x) for x in rng.integers(cu[b], cu[b + 1], 3)]
+    ref = _oracle(inp, rows=rows)
+    got = out.cpu().double().numpy()
+    err = float(np.max(np.abs(got[rows] - ref[rows])))
+    print(f"{name}: {len(rows)} sampled rows, max-abs {err:.3e}", flush=True)
+    assert err <= TOL

@@ -16,6 +16,8 @@ Tensor layouts (all contiguous):
   prefill: q, k, v, rho  [B, H, L, d]   gate [H] fp32
   decode : q, rho        [B, H, d]      kcache, vcache [B, H, Lmax, d]
            seqlens       [B] int32      gate [H] fp32
+  chunk  : q, rho        [T, H, d]      (packed, token-major)
+           kcache, vcache [B, H, Lmax, d]   cu_q [B+1], ctx [B] int32   gate [H] fp32
 """
 from __future__ import annotations
 
@@ -205,3 +207,64 @@ def decode_bytes(seqlens, H, d, elem=2) -> float:
     B = len(sl)
     return (sum(sl) * H * 2 * d * elem + 2 * B * H * d * elem + B * H * d * 4
             + 4 * H + 4 * B)
+
+
+# Chunked prefill against a cache (not among the five numbered workloads):
+# sequences with ctx cached keys each append a chunk of queries.
+CHUNK_WORKLOADS = {
+    "chunk_bf16_B8_H16_ctx4096_q512_d128": dict(B=8, H=16, d=128, ctx=4096, n=512, seed=1101),
+    "chunk_bf16_B32_H16_ctx8192_q16_d128": dict(B=32, H=16, d=128, ctx=8192, n=16, seed=1102),
+}
+
+
+def chunk_inputs(H, d, ctx, n, dtype="bf16", seed=0, device="cpu", rho_std=0.1,
+                 gate=("uniform", 0.2, 1.0), Lmax=None):
+    """Draw a packed chunked-prefill batch.  ctx[b] cached keys and n[b] new
+    queries per sequence; the cache [B, H, Lmax, d] is filled everywhere (rows
+    past ctx[b] + n[b] hold ordinary values a correct kernel never reads),
+    q and rho are N(0,1) and N(0, rho_std^2), token-major [T, H, d].  Returns
+    the tensors plus cu_q, ctx (int32) and max_q."""
+    B = len(ctx)
+    assert len(n) == B
+    Lmax = max(c + m for c, m in zip(ctx, n)) if Lmax is None else Lmax
+    T = sum(n)
+    g = _gen(device, seed)
+    t = DTYPES[dtype]
+    q = _randn((max(T, 1), H, d), g, device)[:T]
+    rho = _randn((max(T, 1), H, d), g, device, std=rho_std)[:T]
+    kc = torch.empty((B, H, Lmax, d), dtype=t, device=device)
+    vc = torch.empty((B, H, Lmax, d), dtype=t, device=device)
+    for b in range(B):
+        kc[b].copy_(_randn((H, Lmax, d), g, device))
+    for b in range(B):
+        vc[b].copy_(_randn((H, Lmax, d), g, device))
+    cu = [0]
+    for m in n:
+        cu.append(cu[-1] + m)
+    gt = _gate(H, gate, g, device)
+    return dict(q=q.to(t).contiguous(), rho=rho.to(t).contiguous(), kcache=kc, vcache=vc,
+                gate=gt, cu_q=torch.tensor(cu, dtype=torch.int32, device=device),
+                ctx=torch.tensor(list(ctx), dtype=torch.int32, device=device),
+                max_q=max(max(n), 1), T=T)
+
+
+def make_chunk_workload(name, device="cpu"):
+    w = CHUNK_WORKLOADS[name]
+    return chunk_inputs(w["H"], w["d"], [w["ctx"]] * w["B"], [w["n"]] * w["B"], "bf16",
+                        w["seed"], device)
+
+
+def chunk_flops(ctx, n, H, d) -> float:
+    """Algorithmic flops of a chunked prefill: 8d per (query, attended key)
+    pair; chunk query j of a sequence attends ctx + j + 1 keys."""
+    pairs = sum(m * c + m * (m + 1) // 2 for c, m in zip(ctx, n))
+    return 8.0 * d * H * pairs
+
+
+def chunk_bytes(ctx, n, H, d, elem=2) -> float:
+    """Algorithmic HBM bytes of a chunked prefill: the cache K and V rows the
+    chunks attend, q and rho in, fp32 out, gate and the two index arrays."""
+    keys = sum(c + m for c, m in zip(ctx, n))
+    T = sum(n)
+    B = len(n)
+    return (keys * H * 2 * d * elem + T * H * d * (2 * elem + 4) + 4 * H + 4 * (2 * B + 1))
