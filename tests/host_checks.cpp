@@ -159,6 +159,62 @@ void softmax_rejections() {
          "softmax decode workspace too small");
 }
 
+// Training, backward and chunked-prefill entry points.
+void training_and_chunk_rejections() {
+  const char* ft = "parallax_prefill_train";
+  expect(parallax_prefill_train(P(0), P(1), P(2), P(3), F(4), F(5), F(6), F(7), F(8), 1, 1, 64, 64,
+                                0.f, PLX_F32, nullptr, 0, nullptr), PLX_EUNSUPPORTED, ft,
+         "train fp32");
+  expect(parallax_prefill_train(P(0), P(1), P(2), P(3), F(4), F(5), nullptr, F(7), F(8), 1, 1, 64,
+                                64, 0.f, PLX_BF16, nullptr, 0, nullptr), PLX_EINVAL, ft,
+         "train null lse");
+  expect(parallax_prefill_train(P(0), P(1), P(2), P(3), F(4), F(5), F(6), F(7), F(8), 1, 1, 64, 96,
+                                0.f, PLX_BF16, nullptr, 0, nullptr), PLX_EUNSUPPORTED, ft,
+         "train d=96");
+  const size_t tw = parallax_prefill_workspace_bytes(2, 1, 100, 64, PLX_BF16);
+  expect(parallax_prefill_train(P(0), P(1), P(2), P(3), F(4), F(5), F(6), F(7), F(8), 2, 1, 100,
+                                64, 0.f, PLX_BF16, P(9), tw - 1, nullptr), PLX_EINVAL, ft,
+         "train workspace too small");
+  const char* fb = "parallax_prefill_backward";
+  check(parallax_prefill_backward_workspace_bytes(2, 3, 100, 128) > 0, "backward workspace > 0");
+  check(parallax_prefill_backward_workspace_bytes(2, 3, 100, 80) == 0, "backward d=80 gives 0");
+  check(parallax_prefill_backward_workspace_bytes(0, 3, 100, 64) == 0, "backward B=0 gives 0");
+  expect(parallax_prefill_backward(P(0), P(1), P(2), P(3), F(4), F(5), F(6), F(7), F(8), F(9),
+                                   F(10), F(11), F(12), F(13), nullptr, 1, 1, 64, 64, 0.f,
+                                   PLX_BF16, nullptr, 0, nullptr), PLX_EINVAL, fb,
+         "backward null dgate");
+  expect(parallax_prefill_backward(P(0), P(1), P(2), P(3), F(4), F(5), F(6), F(7), F(8), F(9),
+                                   F(10), F(11), F(12), F(13), F(14), 1, 1, 64, 64, 0.f, PLX_F32,
+                                   nullptr, 0, nullptr), PLX_EUNSUPPORTED, fb, "backward fp32");
+  const size_t bw = parallax_prefill_backward_workspace_bytes(1, 2, 70, 64);
+  expect(parallax_prefill_backward(P(0), P(1), P(2), P(3), F(4), F(5), F(6), F(7), F(8), F(9),
+                                   F(10), F(11), F(12), F(13), F(14), 1, 2, 70, 64, 0.f,
+                                   PLX_BF16, P(15), bw - 1, nullptr), PLX_EINVAL, fb,
+         "backward workspace too small");
+  const char* fc = "parallax_prefill_chunk";
+  check(parallax_prefill_chunk_workspace_bytes(2, 3, 130, 128) ==
+            parallax_prefill_workspace_bytes(2, 3, 130, 128, PLX_BF16),
+        "chunk workspace = V^T tiles of the cache");
+  expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 0, 64, 8, 64,
+                                0.f, PLX_BF16, nullptr, 0, nullptr), PLX_EINVAL, fc, "chunk T=0");
+  expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 0, 64,
+                                0.f, PLX_BF16, nullptr, 0, nullptr), PLX_EINVAL, fc,
+         "chunk max_q=0");
+  expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), nullptr, I(7), 1, 1, 8, 64, 8,
+                                64, 0.f, PLX_BF16, nullptr, 0, nullptr), PLX_EINVAL, fc,
+         "chunk null cu_q");
+  expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8, 80,
+                                0.f, PLX_BF16, nullptr, 0, nullptr), PLX_EUNSUPPORTED, fc,
+         "chunk d=80");
+  expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8, 64,
+                                0.f, PLX_F32, nullptr, 0, nullptr), PLX_EUNSUPPORTED, fc,
+         "chunk fp32");
+  const size_t cw = parallax_prefill_chunk_workspace_bytes(2, 2, 300, 64);
+  expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 2, 2, 40, 300, 20,
+                                64, 0.f, PLX_BF16, P(8), cw - 1, nullptr), PLX_EINVAL, fc,
+         "chunk workspace too small");
+}
+
 // Without a device, valid arguments reach the HIP runtime: the launch and
 // allocation failures must be reported, not crash.
 void no_device_failures() {
@@ -205,6 +261,25 @@ void no_device_failures() {
   expect(parallax_softmax_decode(P(0), P(1), P(2), F(3), I(4), 1, 1, 64, 128, 0.f, PLX_F32, 0,
                                  nullptr, 0, nullptr), PLX_ENOMEM, "parallax_softmax_decode",
          "softmax decode allocation failure");
+  expect(parallax_prefill_train(P(0), P(1), P(2), P(3), F(4), F(5), F(6), F(7), F(8), 1, 1, 64, 64,
+                                0.f, PLX_BF16, P(9), ws, nullptr), PLX_EHIP,
+         "parallax_prefill_train", "train launch failure");
+  const size_t bws = parallax_prefill_backward_workspace_bytes(1, 1, 64, 64);
+  expect(parallax_prefill_backward(P(0), P(1), P(2), P(3), F(4), F(5), F(6), F(7), F(8), F(9),
+                                   F(10), F(11), F(12), F(13), F(14), 1, 1, 64, 64, 0.f,
+                                   PLX_BF16, P(15), bws, nullptr), PLX_EHIP,
+         "parallax_prefill_backward", "backward launch failure");
+  expect(parallax_prefill_backward(P(0), P(1), P(2), P(3), F(4), F(5), F(6), F(7), F(8), F(9),
+                                   F(10), F(11), F(12), F(13), F(14), 1, 1, 64, 64, 0.f,
+                                   PLX_BF16, nullptr, 0, nullptr), PLX_ENOMEM,
+         "parallax_prefill_backward", "backward allocation failure");
+  const size_t cws = parallax_prefill_chunk_workspace_bytes(1, 1, 64, 64);
+  expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8, 64,
+                                0.f, PLX_BF16, P(8), cws, nullptr), PLX_EHIP,
+         "parallax_prefill_chunk", "chunk launch failure");
+  expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8, 64,
+                                0.f, PLX_BF16, nullptr, 0, nullptr), PLX_ENOMEM,
+         "parallax_prefill_chunk", "chunk allocation failure");
 }
 
 void error_text_is_per_thread() {
@@ -225,6 +300,7 @@ int main() {
   prefill_rejections();
   decode_rejections();
   softmax_rejections();
+  training_and_chunk_rejections();
   error_text_is_per_thread();
   int n_dev = 0;
   if (hipGetDeviceCount(&n_dev) != hipSuccess) n_dev = 0;

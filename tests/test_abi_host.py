@@ -110,6 +110,22 @@ def test_softmax_calls_reject_bad_arguments(lib):
     assert h(x, x, x, x, x, 1, 1, 64, 128, 0.0, 1, 32, NULL, 0, NULL) == PLX_EINVAL
 
 
+def test_training_and_chunk_calls_reject_bad_arguments(lib):
+    x = ctypes.c_void_p(0x1000)
+    t = lib.parallax_prefill_train
+    assert t(x, x, x, x, x, x, x, x, x, 1, 1, 64, 128, 0.0, 0, NULL, 0, NULL) == PLX_EUNSUPPORTED
+    assert t(x, x, x, x, x, x, NULL, x, x, 1, 1, 64, 128, 0.0, 1, NULL, 0, NULL) == PLX_EINVAL
+    b = lib.parallax_prefill_backward
+    args = [x] * 14 + [NULL]
+    assert b(*args, 1, 1, 64, 128, 0.0, 1, NULL, 0, NULL) == PLX_EINVAL
+    assert b(*([x] * 15), 1, 1, 64, 128, 0.0, 0, NULL, 0, NULL) == PLX_EUNSUPPORTED
+    assert lib.parallax_prefill_backward_workspace_bytes(1, 1, 64, 128) > 0
+    c = lib.parallax_prefill_chunk
+    assert c(*([x] * 8), 1, 1, 0, 64, 8, 128, 0.0, 1, NULL, 0, NULL) == PLX_EINVAL
+    assert c(*([x] * 8), 1, 1, 8, 64, 8, 48, 0.0, 1, NULL, 0, NULL) == PLX_EUNSUPPORTED
+    assert c(*([x] * 6), NULL, x, 1, 1, 8, 64, 8, 128, 0.0, 1, NULL, 0, NULL) == PLX_EINVAL
+
+
 def test_binding_raises_without_library(monkeypatch, tmp_path):
     """The product path has no fallback: a missing library is an error."""
     monkeypatch.setattr(_native, "_lib", None)

@@ -154,6 +154,73 @@ def test_softmax_writes_stay_in_bounds(dtype, d):
     _unchanged(inp, snap)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_training_writes_stay_in_bounds(d):
+    """Training forward and backward: guard bands around every output and
+    workspace, every element written, inputs unmodified."""
+    lib = _native.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    B, H, L = 2, 3, 130
+    inp = wl.prefill_inputs(B, H, L, d, "bf16", seed=650 + d, device="cuda", rho_std=0.5,
+                            gate=("uniform", 0.2, 1.0))
+    snap = _snapshot(inp)
+    nf, nr = B * H * L * d * 4, B * H * L * 4
+    bufs = {n: _guarded(nb) for n, nb in (("out", nf), ("lse", nr), ("rbar", nr), ("corr", nf))}
+    fws = lib.parallax_prefill_workspace_bytes(B, H, L, d, _native.PLX_BF16)
+    fbuf, fptr = _guarded(fws)
+    st = lib.parallax_prefill_train(inp["q"].data_ptr(), inp["k"].data_ptr(), inp["v"].data_ptr(),
+                                    inp["rho"].data_ptr(), inp["gate"].data_ptr(),
+                                    *(bufs[n][1] for n in ("out", "lse", "rbar", "corr")),
+                                    B, H, L, d, 0.0, _native.PLX_BF16, fptr, fws, stream)
+    assert st == 0, lib.parallax_last_error()
+    torch.cuda.synchronize()
+    for n, nb in (("out", nf), ("lse", nr), ("rbar", nr), ("corr", nf)):
+        _check_guards(bufs[n][0], nb, "train " + n)
+    _check_guards(fbuf, fws, "train workspace")
+    _unchanged(inp, snap)
+    dout = torch.randn((B, H, L, d), device="cuda")
+    grads = {n: _guarded(nb) for n, nb in (("dq", nf), ("dk", nf), ("dv", nf), ("drho", nf),
+                                          ("dgate", H * 4))}
+    bws = lib.parallax_prefill_backward_workspace_bytes(B, H, L, d)
+    bbuf, bptr = _guarded(bws)
+    saved = [bufs[n][1] for n in ("out", "corr", "lse", "rbar")]
+    st = lib.parallax_prefill_backward(inp["q"].data_ptr(), inp["k"].data_ptr(),
+                                       inp["v"].data_ptr(), inp["rho"].data_ptr(),
+                                       inp["gate"].data_ptr(), *saved, dout.data_ptr(),
+                                       *(grads[n][1] for n in ("dq", "dk", "dv", "drho", "dgate")),
+                                       B, H, L, d, 0.0, _native.PLX_BF16, bptr, bws, stream)
+    assert st == 0, lib.parallax_last_error()
+    torch.cuda.synchronize()
+    for n, nb in (("dq", nf), ("dk", nf), ("dv", nf), ("drho", nf), ("dgate", H * 4)):
+        _check_guards(grads[n][0], nb, "backward " + n)
+    # the workspace holds padded tiles and alignment gaps: only its bounds are checked
+    _check_guards(bbuf, bws, "backward workspace", fully_written=False)
+    _unchanged(inp, snap)
+
+
+def test_chunk_writes_stay_in_bounds():
+    lib = _native.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    ctx, n, H, d = [70, 0, 5], [20, 90, 1], 2, 128
+    inp = wl.chunk_inputs(H, d, ctx, n, seed=660, device="cuda", Lmax=200)
+    snap = _snapshot(inp)
+    T = inp["T"]
+    ob, op = _guarded(T * H * d * 4)
+    ws = lib.parallax_prefill_chunk_workspace_bytes(3, H, 200, d)
+    wb, wp = _guarded(ws)
+    st = lib.parallax_prefill_chunk(inp["q"].data_ptr(), inp["kcache"].data_ptr(),
+                                    inp["vcache"].data_ptr(), inp["rho"].data_ptr(),
+                                    inp["gate"].data_ptr(), op, inp["cu_q"].data_ptr(),
+                                    inp["ctx"].data_ptr(), 3, H, T, 200, inp["max_q"], d, 0.0,
+                                    _native.PLX_BF16, wp, ws, stream)
+    assert st == 0, lib.parallax_last_error()
+    torch.cuda.synchronize()
+    _check_guards(ob, T * H * d * 4, "chunk out")
+    # only the V^T tiles of cache rows the chunks read are staged
+    _check_guards(wb, ws, "chunk workspace", fully_written=False)
+    _unchanged(inp, snap)
+
+
 def test_nan_in_a_query_row_stays_in_that_row():
     """A NaN in one query row turns that output row into NaN.  Rows outside its
     16-row block (one wave) are bit-identical to a clean run; rows inside it
