@@ -5,10 +5,13 @@ Only the test suite, the package smoke check and the benchmark's CPU-baseline
 leg may import this package; the product path never does.
 """
 from .parallax_oracle import (  # noqa: F401
+    conjugate_gradient,
     decode,
     decode_explicit,
     decode_stream,
     explicit_row,
+    lla_prefill,
+    lla_row,
     prefill,
     prefill_explicit,
     prefill_head,

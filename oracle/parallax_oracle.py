@@ -373,3 +373,77 @@ def prefill_chunk(q, kcache, vcache, rho, gate, cu_q, ctx, scale=None, rows=None
                 V = _f64(vcache[b, h, : p + 1])
                 out[t, h] = decode_stream(qf[t, h], K, V, rf[t, h], gf[h], sc)
     return out
+
+
+# ------------------------------------------------------- exact LLA (reference)
+# Section "Problem": exact local-linear attention fits, for every query, a
+# softmax-weighted linear model of the values around q_i; its probe is the
+# solution of a per-token linear system, solved in the original method by
+# parallel conjugate gradients with a regulariser lambda that trades solver
+# stability against collapse to softmax attention.  Section "Core mechanism":
+# Parallax replaces that probe by a learned rho_i and drops the boundary
+# factor eta_i.  Readings (the pages give neither the system nor eta or lambda):
+#   * the system is the ridge-regularised normal equation of the weighted fit,
+#     (Sigma_KK^(i) + lambda I) rho*_i = kbar_i - q_i, with Sigma_KK^(i) the
+#     weighted key covariance (no Bessel factor) and kbar_i the weighted key mean;
+#   * the output is Eq. 2 with that probe and gate 1: o_i = o^SA_i - Sigma_VK rho*_i
+#     (lambda = 0 gives the intercept of the weighted least-squares fit of v on
+#     k - q_i, the local-linear estimate at q_i; lambda -> infinity gives o^SA_i);
+#   * eta_i = 0, as in Parallax.
+# Oracle only: no kernel computes it.
+
+def conjugate_gradient(A, b, iters=None, tol=0.0):
+    """Hestenes-Stiefel conjugate gradients for a symmetric positive definite A,
+    from x = 0, for `iters` steps (default: the dimension, which is exact in
+    exact arithmetic) or until the residual norm is <= tol."""
+    n = b.shape[0]
+    iters = n if iters is None else iters
+    x = np.zeros_like(b)
+    r = b.copy()
+    p = r.copy()
+    rr = float(r @ r)
+    for _ in range(iters):
+        if rr <= tol * tol:
+            break
+        Ap = A @ p
+        alpha = rr / float(p @ Ap)
+        x = x + alpha * p
+        r = r - alpha * Ap
+        rr_new = float(r @ r)
+        p = r + (rr_new / rr) * p
+        rr = rr_new
+    return x
+
+
+def lla_row(q_i, K, V, scale, lam, solver="direct", cg_iters=None):
+    """Exact LLA output for one query over keys K [n, d_k], values V [n, d_v].
+    Returns (o, rho_star)."""
+    q_i, K, V = _f64(q_i), _f64(K), _f64(V)
+    w = softmax_weights(q_i, K, scale)
+    o_sa = w @ V
+    kbar = w @ K
+    Kc = K - kbar
+    s_kk = Kc.T @ (w[:, None] * Kc)
+    s_vk = (V - o_sa).T @ (w[:, None] * Kc)
+    A = s_kk + lam * np.eye(K.shape[1])
+    rhs = kbar - q_i
+    if solver == "cg":
+        rho = conjugate_gradient(A, rhs, cg_iters)
+    else:
+        rho = np.linalg.solve(A, rhs)
+    return o_sa - s_vk @ rho, rho
+
+
+def lla_prefill(q, k, v, lam, scale=None, solver="direct", cg_iters=None):
+    """Causal exact-LLA prefill: q, k [B,H,L,d_k], v [B,H,L,d_v].  lam > 0
+    unless every prefix's key covariance is non-singular."""
+    q, k, v = map(_f64, (q, k, v))
+    B, H, L, dk = q.shape
+    sc = _default_scale(dk, scale)
+    out = np.empty(v.shape)
+    for b in range(B):
+        for h in range(H):
+            for i in range(L):
+                out[b, h, i] = lla_row(q[b, h, i], k[b, h, : i + 1], v[b, h, : i + 1], sc, lam,
+                                       solver, cg_iters)[0]
+    return out
