@@ -68,13 +68,21 @@ template <int D>
 __device__ __forceinline__ int rm_off(int r, int c) {
   return r * D + ((c ^ (r & (D / 8 - 1))) << 3);
 }
-// Transposed tile, one row of W positions per feature (W = 64 or 32).  For
-// W = 64 the chunk swizzle is the forward's V^T swizzle; for W = 32 a row holds
-// four chunks and rows f and f+4 must land in different bank quads.
+// Transposed tile, one row of W positions per feature (W = 64 or 32).  A
+// fragment read takes one 16-byte chunk from each of 16 consecutive rows; eight
+// lanes at a time must hit eight different 16-byte slots of a 128-byte bank
+// line.  For W = 64 (128-byte rows) the chunk swizzle is the forward's V^T
+// swizzle c ^ (f & 7).  For W = 32 a row is half a line: rows f and f+1 fill the
+// two halves, so among the even (or odd) rows of an 8-row group the chunk must
+// differ, c ^ ((f >> 1) & 3).
+template <int W>
+__device__ __forceinline__ int tr_swz(int f) {
+  if constexpr (W == 64) return f & 7;
+  else return (f >> 1) & 3;
+}
 template <int W>
 __device__ __forceinline__ int tr_off(int f, int c) {
-  if constexpr (W == 64) return f * 64 + ((c ^ (f & 7)) << 3);
-  else return f * 32 + ((c ^ ((f >> 2) & 3)) << 3);
+  return f * W + ((c ^ tr_swz<W>(f)) << 3);
 }
 
 // ------------------------------------------------------------------- prep
@@ -266,10 +274,10 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     {
       const int f = e / BW_BQ, pc = (e % BW_BQ) / 8;
-      // logical chunk c sits at physical chunk c ^ ((f >> 2) & 3); the global
-      // tile row of feature f holds 64 positions, this step's 32 start at
-      // the half selected by the base pointer
-      troff[i] = (uint32_t)((f * BW_T + ((pc ^ ((f >> 2) & 3)) << 3)) * 2);
+      // physical chunk pc of LDS row f holds logical chunk pc ^ tr_swz(f); the
+      // global tile row of feature f holds 64 positions, this step's 32 start
+      // at the half selected by the base pointer
+      troff[i] = (uint32_t)((f * BW_T + ((pc ^ tr_swz<BW_BQ>(f)) << 3)) * 2);
     }
   }
   const int n_qs = (L + BW_BQ - 1) / BW_BQ;
@@ -479,7 +487,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     {
       const int f = e / BW_T, pc = (e % BW_T) / 8;
-      troff[i] = (uint32_t)((f * BW_T + ((pc ^ (f & 7)) << 3)) * 2);
+      troff[i] = (uint32_t)((f * BW_T + ((pc ^ tr_swz<BW_T>(f)) << 3)) * 2);
     }
   }
   const int last_q = min(q0 + BR, L) - 1;
