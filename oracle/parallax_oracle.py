@@ -19,7 +19,7 @@ Modeling" (technical summary, Korean and German editions on gist.science):
     attention (the rho = 0 special case);
   * section "Results": a gate value scales the correction branch.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * Sigma_KV^(i) is the cross-covariance of values and keys under the causal
     softmax weights w_ij of query i, centred at the weighted means, weights
     summing to one, no Bessel factor; it is d_v x d_k so that it acts on
