@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 4
+#define PARALLAX_ABI_VERSION 5
 
 typedef enum {
   PLX_OK = 0,
@@ -176,6 +176,29 @@ int parallax_prefill_chunk(const void* q, const void* kcache, const void* vcache
                            const int32_t* cu_q, const int32_t* ctx, int B, int H, int T,
                            int Lmax, int max_q, int d, float scale, int dtype,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* A serving loop can keep the V cache's staged copy and skip the per-call
+ * staging, which for short chunks is most of the traffic: vt_cache
+ * ([B, H, ceil(Lmax/64), d, 64] fp16, parallax_prefill_chunk_workspace_bytes()
+ * bytes, the layout of parallax_prefill_stage_v applied to the cache) holds
+ * V^T of every cache row.
+ * parallax_stage_v_rows: after the chunks' values are written to vcache,
+ *   re-stages only the 64-row tiles that hold rows ctx[b] .. ctx[b]+n_b-1
+ *   (arguments and clamping as in parallax_prefill_chunk); rows at or past
+ *   ctx[b]+n_b of those tiles are written as zeros.
+ * parallax_prefill_chunk_vt: parallax_prefill_chunk reading V from vt_cache,
+ *   whose tiles must hold rows 0 .. ctx[b]+n_b-1 of each sequence (after
+ *   parallax_stage_v_rows for every append, or one parallax_prefill_stage_v of
+ *   a cache whose rows are all finite).  Results are bit-identical to
+ *   parallax_prefill_chunk. */
+int parallax_stage_v_rows(const void* vcache, void* vt_cache, const int32_t* cu_q,
+                          const int32_t* ctx, int B, int H, int T, int Lmax, int max_q, int d,
+                          void* stream);
+
+int parallax_prefill_chunk_vt(const void* q, const void* kcache, const void* vt_cache,
+                              const void* rho, const float* gate, float* out,
+                              const int32_t* cu_q, const int32_t* ctx, int B, int H, int T,
+                              int Lmax, int max_q, int d, float scale, int dtype, void* stream);
 
 /* --------------------------------------------------------- softmax baseline
  * Plain causal softmax attention, o_i = o^SA_i (Eq. 2 without the correction

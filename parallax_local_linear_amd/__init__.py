@@ -27,7 +27,8 @@ __all__ = ["prefill", "decode", "prefill_stage_v", "prefill_attend", "decode_par
            "decode_combine", "prefill_workspace_bytes", "decode_workspace_bytes",
            "decode_default_split", "softmax_prefill", "softmax_prefill_attend",
            "softmax_decode", "prefill_train", "prefill_backward",
-           "prefill_backward_workspace_bytes", "prefill_chunk", "ParallaxError"]
+           "prefill_backward_workspace_bytes", "prefill_chunk", "stage_v_rows",
+           "chunk_vt_cache", "ParallaxError"]
 
 _DT = {torch.bfloat16: PLX_BF16, torch.float32: PLX_F32}
 
@@ -188,12 +189,7 @@ def prefill_backward(q, k, v, rho, gate, out, corr, lse, rbar, dout, scale=None,
     return grads
 
 
-def prefill_chunk(q, kcache, vcache, rho, gate, cu_q, ctx, max_q, scale=None, out=None,
-                  workspace=None):
-    """Chunked causal prefill against a KV cache (bf16).  q, rho: [T, H, d]
-    packed token-major; kcache, vcache: [B, H, Lmax, d] holding each chunk's
-    own keys at positions ctx[b] .. ctx[b]+n_b-1; cu_q [B+1] and ctx [B] int32 on
-    the GPU; max_q >= the largest chunk.  Returns out [T, H, d] fp32."""
+def _chunk_checks(q, kcache, rho, gate, cu_q, ctx):
     _check("q", q, torch.bfloat16)
     _check("kcache", kcache, torch.bfloat16)
     if q.dim() != 3 or kcache.dim() != 4:
@@ -201,14 +197,59 @@ def prefill_chunk(q, kcache, vcache, rho, gate, cu_q, ctx, max_q, scale=None, ou
     T, H, d = q.shape
     B, _, Lmax, _ = kcache.shape
     _check("kcache", kcache, torch.bfloat16, (B, H, Lmax, d), q.device)
-    _check("vcache", vcache, torch.bfloat16, (B, H, Lmax, d), q.device)
     _check("rho", rho, torch.bfloat16, (T, H, d), q.device)
     _check("gate", gate, torch.float32, (H,), q.device)
     _check("cu_q", cu_q, torch.int32, (B + 1,), q.device)
     _check("ctx", ctx, torch.int32, (B,), q.device)
+    return T, H, d, B, Lmax
+
+
+def chunk_vt_cache(B, H, Lmax, d, device):
+    """An empty staged V^T cache for prefill_chunk(..., vt_cache=...)."""
+    n = int(lib().parallax_prefill_chunk_workspace_bytes(B, H, Lmax, d))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def stage_v_rows(vcache, vt_cache, cu_q, ctx, max_q, T):
+    """Re-stage into vt_cache the V^T tiles holding rows ctx[b] .. ctx[b]+n_b-1
+    of vcache [B, H, Lmax, d] (after those rows were written)."""
+    _check("vcache", vcache, torch.bfloat16)
+    if vcache.dim() != 4:
+        raise ValueError("vcache must be [B, H, Lmax, d]")
+    B, H, Lmax, d = vcache.shape
+    _check("vt_cache", vt_cache, device=vcache.device)
+    if vt_cache.numel() * vt_cache.element_size() < int(
+            lib().parallax_prefill_chunk_workspace_bytes(B, H, Lmax, d)):
+        raise ValueError("vt_cache is too small")
+    _check("cu_q", cu_q, torch.int32, (B + 1,), vcache.device)
+    _check("ctx", ctx, torch.int32, (B,), vcache.device)
+    _launch(vcache.device, "parallax_stage_v_rows", _ptr(vcache), _ptr(vt_cache), _ptr(cu_q),
+            _ptr(ctx), B, H, int(T), Lmax, int(max_q), d)
+    return vt_cache
+
+
+def prefill_chunk(q, kcache, vcache, rho, gate, cu_q, ctx, max_q, scale=None, out=None,
+                  workspace=None, vt_cache=None):
+    """Chunked causal prefill against a KV cache (bf16).  q, rho: [T, H, d]
+    packed token-major; kcache, vcache: [B, H, Lmax, d] holding each chunk's
+    own keys at positions ctx[b] .. ctx[b]+n_b-1; cu_q [B+1] and ctx [B] int32 on
+    the GPU; max_q >= the largest chunk.  With vt_cache (kept up to date by
+    stage_v_rows) V is read from the staged cache and vcache may be None.
+    Returns out [T, H, d] fp32."""
+    T, H, d, B, Lmax = _chunk_checks(q, kcache, rho, gate, cu_q, ctx)
     if out is None:
         out = torch.empty((T, H, d), dtype=torch.float32, device=q.device)
     _check("out", out, torch.float32, (T, H, d), q.device)
+    if vt_cache is not None:
+        _check("vt_cache", vt_cache, device=q.device)
+        if vt_cache.numel() * vt_cache.element_size() < int(
+                lib().parallax_prefill_chunk_workspace_bytes(B, H, Lmax, d)):
+            raise ValueError("vt_cache is too small")
+        _launch(q.device, "parallax_prefill_chunk_vt", _ptr(q), _ptr(kcache), _ptr(vt_cache),
+                _ptr(rho), _ptr(gate), _ptr(out), _ptr(cu_q), _ptr(ctx), B, H, T, Lmax,
+                int(max_q), d, _scale(scale, d), PLX_BF16)
+        return out
+    _check("vcache", vcache, torch.bfloat16, (B, H, Lmax, d), q.device)
     wsb = int(lib().parallax_prefill_chunk_workspace_bytes(B, H, Lmax, d))
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)

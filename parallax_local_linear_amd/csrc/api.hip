@@ -40,6 +40,9 @@ hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, c
                                 const float* gate, float* out, const int* cu_q, const int* ctx,
                                 int B, int H, int T, int Lmax, int max_q, int d, float scale,
                                 void* vt, hipStream_t s);
+hipError_t launch_stage_v_rows(const void* vc, void* vt, const int* cu_q, const int* ctx, int B,
+                               int H, int T, int Lmax, int max_q, int d, bool new_rows_only,
+                               hipStream_t s);
 }  // namespace plx
 
 namespace {
@@ -82,6 +85,20 @@ bool dims_ok(int B, int H, int L, int d, const char* fn, const char* lname, int*
   }
   if ((long long)B * H * (long long)L * d > kMaxElems || (long long)L * d > (1LL << 31)) {
     *status = fail(PLX_EINVAL, "%s: tensor too large", fn);
+    return false;
+  }
+  return true;
+}
+
+// Checks shared by the chunked-prefill calls.
+bool chunk_args_ok(int B, int H, int T, int Lmax, int max_q, int d, const char* fn, int* st) {
+  if (!dims_ok(B, H, Lmax, d, fn, "Lmax", st)) return false;
+  if (T <= 0 || max_q <= 0) {
+    *st = fail(PLX_EINVAL, "%s: T and max_q must be positive (got %d, %d)", fn, T, max_q);
+    return false;
+  }
+  if ((long long)T * H * d > kMaxElems) {
+    *st = fail(PLX_EINVAL, "%s: tensor too large", fn);
     return false;
   }
   return true;
@@ -408,12 +425,9 @@ int parallax_prefill_chunk(const void* q, const void* kcache, const void* vcache
                            void* stream) {
   const char* fn = "parallax_prefill_chunk";
   int st = PLX_OK;
-  if (!dims_ok(B, H, Lmax, d, fn, "Lmax", &st)) return st;
+  if (!chunk_args_ok(B, H, T, Lmax, max_q, d, fn, &st)) return st;
   if (!dtype_ok(dtype, fn, &st)) return st;
   if (dtype != PLX_BF16) return fail(PLX_EUNSUPPORTED, "%s: only PLX_BF16 is supported", fn);
-  if (T <= 0 || max_q <= 0)
-    return fail(PLX_EINVAL, "%s: T and max_q must be positive (got %d, %d)", fn, T, max_q);
-  if ((long long)T * H * d > kMaxElems) return fail(PLX_EINVAL, "%s: tensor too large", fn);
   if (!q || !kcache || !vcache || !rho || !gate || !out || !cu_q || !ctx)
     return fail(PLX_EINVAL, "%s: null pointer", fn);
   hipStream_t s = (hipStream_t)stream;
@@ -424,6 +438,37 @@ int parallax_prefill_chunk(const void* q, const void* kcache, const void* vcache
     return st;
   hipError_t e = plx::launch_prefill_chunk(q, kcache, vcache, rho, gate, out, cu_q, ctx, B, H, T,
                                            Lmax, max_q, d, eff_scale(scale, d), ws, s);
+  if (e != hipSuccess) return launch_fail(fn, "chunk", e);
+  return ok();
+}
+
+int parallax_stage_v_rows(const void* vcache, void* vt_cache, const int32_t* cu_q,
+                          const int32_t* ctx, int B, int H, int T, int Lmax, int max_q, int d,
+                          void* stream) {
+  const char* fn = "parallax_stage_v_rows";
+  int st = PLX_OK;
+  if (!chunk_args_ok(B, H, T, Lmax, max_q, d, fn, &st)) return st;
+  if (!vcache || !vt_cache || !cu_q || !ctx) return fail(PLX_EINVAL, "%s: null pointer", fn);
+  hipError_t e = plx::launch_stage_v_rows(vcache, vt_cache, cu_q, ctx, B, H, T, Lmax, max_q, d,
+                                          true, (hipStream_t)stream);
+  if (e != hipSuccess) return launch_fail(fn, "stage_v", e);
+  return ok();
+}
+
+int parallax_prefill_chunk_vt(const void* q, const void* kcache, const void* vt_cache,
+                              const void* rho, const float* gate, float* out,
+                              const int32_t* cu_q, const int32_t* ctx, int B, int H, int T,
+                              int Lmax, int max_q, int d, float scale, int dtype, void* stream) {
+  const char* fn = "parallax_prefill_chunk_vt";
+  int st = PLX_OK;
+  if (!chunk_args_ok(B, H, T, Lmax, max_q, d, fn, &st)) return st;
+  if (!dtype_ok(dtype, fn, &st)) return st;
+  if (dtype != PLX_BF16) return fail(PLX_EUNSUPPORTED, "%s: only PLX_BF16 is supported", fn);
+  if (!q || !kcache || !vt_cache || !rho || !gate || !out || !cu_q || !ctx)
+    return fail(PLX_EINVAL, "%s: null pointer", fn);
+  hipError_t e = plx::launch_prefill_chunk(q, kcache, nullptr, rho, gate, out, cu_q, ctx, B, H, T,
+                                           Lmax, max_q, d, eff_scale(scale, d),
+                                           const_cast<void*>(vt_cache), (hipStream_t)stream);
   if (e != hipSuccess) return launch_fail(fn, "chunk", e);
   return ok();
 }

@@ -133,6 +133,7 @@ struct ChunkArgs {
   int Lmax;     // cache rows per (b, h)
   int max_q;    // largest chunk: the grid covers ceil(max_q / queries per workgroup)
   int n64max;   // staged V^T tiles per (b, h): ceil(Lmax / 64)
+  int new_rows_only;   // staging: only the tiles that hold cache rows >= ctx[b]
 };
 // (first row, queries, position of query 0) of sequence b, clamped
 __device__ __forceinline__ void chunk_geometry(const ChunkArgs& ca, int b, int* c0, int* n_q,
@@ -540,6 +541,7 @@ void stage_v_kernel(const __bf16* __restrict__ v, TOUT* __restrict__ vt, int L, 
     chunk_geometry(ca, bh / H, &c0, &n_q, &pos0);
     n_valid = pos0 + n_q;
     if (kt * PF_BC >= n_valid) return;  // uniform over the workgroup
+    if (ca.new_rows_only && kt < pos0 / PF_BC) return;
   }
   const __bf16* src = v + ((size_t)bh * L + (size_t)kt * PF_BC) * D;
   constexpr int CH = PF_BC * D / 8;
@@ -639,14 +641,14 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* vt, con
   return launch_prefill_c<false>(q, k, vt, rho, gate, out, B, H, L, d, sl2, s);
 }
 
-// Chunked prefill: stage V^T of the cache rows each chunk reads, then attend.
-hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, const void* rho,
-                                const float* gate, float* out, const int* cu_q, const int* ctx,
-                                int B, int H, int T, int Lmax, int max_q, int d, float scale,
-                                void* vt, hipStream_t s) {
-  const float sl2 = scale * kLog2e;
+// V^T tiles of the cache rows the chunks read (all of them, or with
+// new_rows_only only the tiles holding rows ctx[b] .. ctx[b]+n_b-1); rows at or
+// past ctx[b]+n_b of a written tile are zero.
+hipError_t launch_stage_v_rows(const void* vc, void* vt, const int* cu_q, const int* ctx, int B,
+                               int H, int T, int Lmax, int max_q, int d, bool new_rows_only,
+                               hipStream_t s) {
   const int n64 = (Lmax + PF_BC - 1) / PF_BC;
-  const ChunkArgs ca{cu_q, ctx, T, Lmax, max_q, n64};
+  const ChunkArgs ca{cu_q, ctx, T, Lmax, max_q, n64, new_rows_only ? 1 : 0};
   const dim3 grid((unsigned)(B * H * n64));
   if (d == 128)
     hipLaunchKernelGGL((stage_v_kernel<128, _Float16, true>), grid, dim3(256), 0, s,
@@ -654,8 +656,22 @@ hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, c
   else
     hipLaunchKernelGGL((stage_v_kernel<64, _Float16, true>), grid, dim3(256), 0, s,
                        (const __bf16*)vc, (_Float16*)vt, Lmax, n64, ca, H);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+// Chunked prefill: unless the caller keeps the V cache staged (vc == null),
+// stage V^T of the cache rows each chunk reads into vt; then attend.
+hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, const void* rho,
+                                const float* gate, float* out, const int* cu_q, const int* ctx,
+                                int B, int H, int T, int Lmax, int max_q, int d, float scale,
+                                void* vt, hipStream_t s) {
+  const float sl2 = scale * kLog2e;
+  const int n64 = (Lmax + PF_BC - 1) / PF_BC;
+  const ChunkArgs ca{cu_q, ctx, T, Lmax, max_q, n64, 0};
+  if (vc) {
+    hipError_t e = launch_stage_v_rows(vc, vt, cu_q, ctx, B, H, T, Lmax, max_q, d, false, s);
+    if (e != hipSuccess) return e;
+  }
   if (d == 128)
     return launch_prefill_t<128, PLX_PF_NW_D128, (PLX_PF_PIPE_D128 != 0), true, false, true>(
         q, kc, vt, rho, gate, out, B, H, Lmax, sl2, s, {}, ca);

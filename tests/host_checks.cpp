@@ -209,6 +209,16 @@ void training_and_chunk_rejections() {
   expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8, 64,
                                 0.f, PLX_F32, nullptr, 0, nullptr), PLX_EUNSUPPORTED, fc,
          "chunk fp32");
+  expect(parallax_stage_v_rows(nullptr, P(1), I(2), I(3), 1, 1, 8, 64, 8, 64, nullptr), PLX_EINVAL,
+         "parallax_stage_v_rows", "stage rows null vcache");
+  expect(parallax_stage_v_rows(P(0), P(1), I(2), I(3), 1, 1, 0, 64, 8, 64, nullptr), PLX_EINVAL,
+         "parallax_stage_v_rows", "stage rows T=0");
+  expect(parallax_prefill_chunk_vt(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8,
+                                   64, 0.f, PLX_F32, nullptr), PLX_EUNSUPPORTED,
+         "parallax_prefill_chunk_vt", "chunk_vt fp32");
+  expect(parallax_prefill_chunk_vt(P(0), P(1), nullptr, P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64,
+                                   8, 64, 0.f, PLX_BF16, nullptr), PLX_EINVAL,
+         "parallax_prefill_chunk_vt", "chunk_vt null vt_cache");
   const size_t cw = parallax_prefill_chunk_workspace_bytes(2, 2, 300, 64);
   expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 2, 2, 40, 300, 20,
                                 64, 0.f, PLX_BF16, P(8), cw - 1, nullptr), PLX_EINVAL, fc,
@@ -280,6 +290,11 @@ void no_device_failures() {
   expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8, 64,
                                 0.f, PLX_BF16, nullptr, 0, nullptr), PLX_ENOMEM,
          "parallax_prefill_chunk", "chunk allocation failure");
+  expect(parallax_stage_v_rows(P(0), P(1), I(2), I(3), 1, 1, 8, 64, 8, 64, nullptr), PLX_EHIP,
+         "parallax_stage_v_rows", "stage rows launch failure");
+  expect(parallax_prefill_chunk_vt(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8,
+                                   64, 0.f, PLX_BF16, nullptr), PLX_EHIP,
+         "parallax_prefill_chunk_vt", "chunk_vt launch failure");
 }
 
 void error_text_is_per_thread() {

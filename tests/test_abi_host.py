@@ -124,6 +124,12 @@ def test_training_and_chunk_calls_reject_bad_arguments(lib):
     assert c(*([x] * 8), 1, 1, 0, 64, 8, 128, 0.0, 1, NULL, 0, NULL) == PLX_EINVAL
     assert c(*([x] * 8), 1, 1, 8, 64, 8, 48, 0.0, 1, NULL, 0, NULL) == PLX_EUNSUPPORTED
     assert c(*([x] * 6), NULL, x, 1, 1, 8, 64, 8, 128, 0.0, 1, NULL, 0, NULL) == PLX_EINVAL
+    sr = lib.parallax_stage_v_rows
+    assert sr(x, NULL, x, x, 1, 1, 8, 64, 8, 128, NULL) == PLX_EINVAL
+    assert sr(x, x, x, x, 1, 1, 8, 64, 8, 96, NULL) == PLX_EUNSUPPORTED
+    cv = lib.parallax_prefill_chunk_vt
+    assert cv(*([x] * 8), 1, 1, 8, 64, 0, 128, 0.0, 1, NULL) == PLX_EINVAL
+    assert cv(*([x] * 8), 1, 1, 8, 64, 8, 128, 0.0, 0, NULL) == PLX_EUNSUPPORTED
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):

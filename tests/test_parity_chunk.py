@@ -117,3 +117,65 @@ def test_chunk_workload_sampled(name):
     err = float(np.max(np.abs(got[rows] - ref[rows])))
     print(f"{name}: {len(rows)} sampled rows, max-abs {err:.3e}", flush=True)
     assert err <= TOL
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", CASES[2:6], ids=lambda c: "ctx" + "-".join(map(str, c[0])))
+def test_staged_cache_matches_per_call_staging(case, d):
+    """V read from a caller-kept staged cache gives the same bits as the call
+    that stages the rows it reads."""
+    plx = _plx()
+    ctx, n = case
+    inp = wl.chunk_inputs(3, d, ctx, n, seed=1400 + sum(ctx) + d, device="cuda", rho_std=0.5)
+    ref = _run(inp)
+    vt = plx.prefill_stage_v(inp["vcache"])
+    out = plx.prefill_chunk(inp["q"], inp["kcache"], None, inp["rho"], inp["gate"], inp["cu_q"],
+                            inp["ctx"], inp["max_q"], vt_cache=vt)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_incremental_serving_with_a_staged_cache(d):
+    """Three rounds of appended chunks: the new K/V rows are written into the
+    caches (whose unwritten rows hold NaN), stage_v_rows re-stages only their
+    tiles, and the chunk reads the staged cache.  Every round matches the
+    oracle and the per-call-staging path bit for bit."""
+    plx = _plx()
+    H, Lmax, B = 2, 400, 3
+    g = torch.Generator(device="cuda").manual_seed(1500 + d)
+    kc = torch.full((B, H, Lmax, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    vt = plx.chunk_vt_cache(B, H, Lmax, d, "cuda")
+    gate = torch.rand(H, generator=g, device="cuda") * 0.8 + 0.2
+    ctx = [0, 37, 100]
+    # rows already cached before the first round, staged like an append from 0
+    for b in range(B):
+        kc[b, :, :ctx[b]] = torch.randn((H, ctx[b], d), generator=g, device="cuda").to(torch.bfloat16)
+        vc[b, :, :ctx[b]] = torch.randn((H, ctx[b], d), generator=g, device="cuda").to(torch.bfloat16)
+    cu0 = torch.tensor([0] + list(np.cumsum(ctx)), dtype=torch.int32, device="cuda")
+    zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+    plx.stage_v_rows(vc, vt, cu0, zero, max(ctx), int(sum(ctx)))
+    for n in ([5, 64, 17], [1, 1, 80], [70, 3, 0]):
+        for b in range(B):
+            kc[b, :, ctx[b]:ctx[b] + n[b]] = torch.randn((H, n[b], d), generator=g,
+                                                        device="cuda").to(torch.bfloat16)
+            vc[b, :, ctx[b]:ctx[b] + n[b]] = torch.randn((H, n[b], d), generator=g,
+                                                        device="cuda").to(torch.bfloat16)
+        T = sum(n)
+        q = torch.randn((T, H, d), generator=g, device="cuda").to(torch.bfloat16)
+        rho = (0.5 * torch.randn((T, H, d), generator=g, device="cuda")).to(torch.bfloat16)
+        cu = torch.tensor([0] + list(np.cumsum(n)), dtype=torch.int32, device="cuda")
+        cx = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+        plx.stage_v_rows(vc, vt, cu, cx, max(n), T)
+        out = plx.prefill_chunk(q, kc, None, rho, gate, cu, cx, max(n), vt_cache=vt)
+        ref = plx.prefill_chunk(q, kc, vc, rho, gate, cu, cx, max(n))
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(out).all())
+        assert torch.equal(out, ref)
+        want = po.prefill_chunk(q.cpu(), kc.cpu(), vc.cpu(), rho.cpu(), gate.cpu(), cu.cpu(),
+                                cx.cpu())
+        err = float(np.max(np.abs(out.cpu().double().numpy() - want)))
+        print(f"serving d{d} ctx{ctx} n{n}: max-abs {err:.3e}", flush=True)
+        assert err <= TOL
+        ctx = [c + m for c, m in zip(ctx, n)]
