@@ -28,7 +28,8 @@ __all__ = ["prefill", "decode", "prefill_stage_v", "prefill_attend", "decode_par
            "decode_default_split", "softmax_prefill", "softmax_prefill_attend",
            "softmax_decode", "prefill_train", "prefill_backward",
            "prefill_backward_workspace_bytes", "prefill_chunk", "stage_v_rows",
-           "chunk_vt_cache", "ParallaxError"]
+           "chunk_vt_cache", "parallax_attention", "ParallaxAttentionFunction",
+           "ParallaxError"]
 
 _DT = {torch.bfloat16: PLX_BF16, torch.float32: PLX_F32}
 
@@ -407,3 +408,30 @@ def decode_combine(partials, gate, seqlens, Lmax, split_keys, out=None):
     _launch(partials.device, "parallax_decode_combine", _ptr(partials), _ptr(gate),
             _ptr(seqlens), _ptr(out), B, H, Lmax, d, split_keys)
     return out
+
+
+class ParallaxAttentionFunction(torch.autograd.Function):
+    """Autograd wrapper of the causal bf16 prefill: the forward pass runs
+    prefill_train (saving lse, rbar and the correction vector), the backward
+    pass runs prefill_backward.  Gradients come back in the inputs' dtypes."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, rho, gate, scale):
+        out, lse, rbar, corr = prefill_train(q, k, v, rho, gate, scale=scale)
+        ctx.save_for_backward(q, k, v, rho, gate, out, corr, lse, rbar)
+        ctx.scale = scale
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, rho, gate, out, corr, lse, rbar = ctx.saved_tensors
+        dq, dk, dv, drho, dgate = prefill_backward(q, k, v, rho, gate, out, corr, lse, rbar,
+                                                   dout.contiguous(), scale=ctx.scale)
+        return (dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), drho.to(rho.dtype),
+                dgate.to(gate.dtype), None)
+
+
+def parallax_attention(q, k, v, rho, gate, scale=None):
+    """Differentiable causal Parallax attention (bf16 q, k, v, rho [B,H,L,d];
+    fp32 gate [H]).  Returns out [B,H,L,d] fp32."""
+    return ParallaxAttentionFunction.apply(q, k, v, rho, gate, scale)

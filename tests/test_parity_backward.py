@@ -152,3 +152,27 @@ def test_backward_full_workload_sampled(wid):
         e = abs(float(grads[4][0]) - dg0) / max(1.0, abs(dg0))
         print(f"workload 2 dgate[0]: {float(grads[4][0]):.6e} vs {dg0:.6e} (rel {e:.2e})", flush=True)
         assert e <= 2e-2
+
+
+def test_autograd_function_matches_the_oracle():
+    """torch autograd through parallax_attention: a loss on the output flows to
+    q, k, v, rho (bf16) and the gate (fp32), matching the oracle's gradients of
+    the same loss.  The op after the attention is affine, so the upstream
+    gradient (2 w) is known without the GPU's output."""
+    plx = _plx()
+    B, H, L, d = 1, 2, 97, 64
+    inp = wl.prefill_inputs(B, H, L, d, "bf16", seed=990, device="cuda", rho_std=0.5,
+                            gate=("uniform", 0.2, 1.0))
+    leaves = {n: inp[n].clone().requires_grad_(True) for n in ("q", "k", "v", "rho", "gate")}
+    w = _dout((B, H, L, d), 991)
+    out = plx.parallax_attention(leaves["q"], leaves["k"], leaves["v"], leaves["rho"],
+                                 leaves["gate"])
+    loss = ((2.0 * out + 3.0) * w).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    h = {n: inp[n].cpu() for n in inp}
+    ref = po.prefill_backward(h["q"], h["k"], h["v"], h["rho"], h["gate"], 2.0 * w.cpu())
+    for n, key in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("rho", "drho"), ("gate", "dgate")):
+        g = leaves[n].grad
+        assert g is not None and g.dtype == leaves[n].dtype, n
+        assert _rel_err(_np(g), ref[key]) <= 2e-2, n
