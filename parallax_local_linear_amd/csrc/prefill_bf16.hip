@@ -20,7 +20,9 @@
 //   * In the transposed layout a lane owns one query and 4 keys per block, so
 //     the online-softmax row max is lane-local except for two exchanges across
 //     the four lanes that share a query.
-//   * P = exp2(S*scale*log2e - m) and T = P*R are rounded to fp16 (RNE) and fed,
+//   * P = exp2(S*scale*log2e - m) and R are rounded to fp16 (RNE) and T = P*R is
+//     formed from the rounded values by packed fp16 multiplies (half the vector
+//     instructions of an fp32 product followed by a conversion).  P and T are fed,
 //     as B operands, to v_mfma_f32_16x16x32_f16 against the V^T fragment:
 //     O^T += V^T P^T and A_r^T += V^T T^T, fp32 accumulators in registers.  The
 //     row sums l = sum P and c = sum T come from the same rounded values, by one
@@ -381,17 +383,17 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     const uint16_t* vs = smem + 2 * LY::K_ELEMS + (int)vbuf * LY::V_ELEMS;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      f16x8 pf, tf;
+      f16x8 pf, rf, tf;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sa[2 * t + hh][j], sl2, -m_use));
-          const float tv = CORR ? p * ra[2 * t + hh][j] : 0.f;
-          pf[4 * hh + j] = (_Float16)p;
-          if constexpr (CORR) tf[4 * hh + j] = (_Float16)tv;
+          pf[4 * hh + j] =
+              (_Float16)__builtin_amdgcn_exp2f(fmaf(sa[2 * t + hh][j], sl2, -m_use));
+          if constexpr (CORR) rf[4 * hh + j] = (_Float16)ra[2 * t + hh][j];
         }
       }
+      if constexpr (CORR) tf = pf * rf;
       acc_l = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8, pf, acc_l, 0, 0, 0);
       if constexpr (CORR)
         acc_c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8, tf, acc_c, 0, 0, 0);
