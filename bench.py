@@ -20,10 +20,12 @@ decode and the d=64 prefill) are timed too and reported under "extra".
 the gradient needs) and the backward pass on the prefill workloads; its
 TFLOP/s count 16*d flops per causal pair (S and R recomputed, dO V^T, and the
 dV, dK (two), dQ and drho products), twice the forward's 8*d.
-"chunk" times the chunked prefill against a KV cache on two shapes: long
-chunks on a 4096-key context (TFLOP/s) and 16-query chunks on an 8192-key
-context (HBM GB/s of the cache rows read); "staged_cache" is the serving loop
-that keeps the staged V cache and re-stages only the appended rows' tiles.
+"chunk" times the chunked prefill against a KV cache on three shapes: long
+chunks on a 4096-key context (TFLOP/s), and 16-query chunks on an 8192-key
+context for 32 and for 2 sequences (HBM GB/s of the cache rows read; the
+2-sequence case runs split-KV, "split_keys" per range); "staged_cache" is the
+serving loop that keeps the staged V cache and re-stages only the appended
+rows' tiles.
 "softmax_relative" times the same kernels with the correction branch compiled
 out (plain causal softmax attention) against the Parallax kernels on each
 workload, alternating the two launch by launch, and reports the time ratio.
@@ -320,8 +322,11 @@ def chunk_block(torch, plx, wl, name, dev, steps=10):
     inp = wl.make_chunk_workload(name, device=dev)
     B, H, d = cw["B"], cw["H"], cw["d"]
     Lmax = inp["kcache"].shape[2]
-    ws = torch.empty(int(plx.lib().parallax_prefill_chunk_workspace_bytes(B, H, Lmax, d)),
+    T, mq = inp["T"], inp["max_q"]
+    ws = torch.empty(int(plx.lib().parallax_prefill_chunk_workspace_bytes(B, H, T, Lmax, mq, d, 0)),
                      dtype=torch.uint8, device=dev)
+    rn = int(plx.lib().parallax_prefill_chunk_vt_workspace_bytes(B, H, T, Lmax, mq, d, 0))
+    rws = torch.empty(rn, dtype=torch.uint8, device=dev) if rn else None
     out = torch.empty((inp["T"], H, d), dtype=torch.float32, device=dev)
     tm = Timer(torch)
     for _ in range(steps + 2):
@@ -339,18 +344,21 @@ def chunk_block(torch, plx, wl, name, dev, steps=10):
                                                    inp["max_q"], inp["T"]),
                                   plx.prefill_chunk(inp["q"], inp["kcache"], None, inp["rho"],
                                                     inp["gate"], inp["cu_q"], inp["ctx"],
-                                                    inp["max_q"], out=out, vt_cache=vt)))
+                                                    inp["max_q"], out=out, vt_cache=vt,
+                                                    workspace=rws)))
     torch.cuda.synchronize()
     ms_st = tm.ms("staged", 2)
     ctx, n = [cw["ctx"]] * B, [cw["n"]] * B
     fl = wl.chunk_flops(ctx, n, H, d)
     nb = wl.chunk_bytes(ctx, n, H, d)
-    res = {"workload": name, "ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 2),
+    split = plx.chunk_default_split(B, H, Lmax, mq, d)
+    res = {"workload": name, "split_keys": split if split < Lmax else None,
+           "ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 2),
            "GB/s": round(nb / ms / 1e6, 1),
            "staged_cache": {"ms": round(ms_st, 4), "TFLOP/s": round(fl / ms_st / 1e9, 2),
                             "GB/s": round(nb / ms_st / 1e6, 1)},
            "flops": fl, "bytes": nb}
-    del inp, ws, out, vt
+    del inp, ws, out, vt, rws
     torch.cuda.empty_cache()
     return res
 

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 5
+#define PARALLAX_ABI_VERSION 6
 
 typedef enum {
   PLX_OK = 0,
@@ -76,8 +76,9 @@ const char* parallax_last_error(void);
  * holds V converted to fp16 in a per-64-key-tile transposed layout (see
  * parallax_prefill_stage_v); the conversion is exact for |v| in
  * [2^-14, 65504] and values must stay below 65504 in magnitude.  The bf16 path
- * rounds the softmax numerators P (kept <= 16) and T = P*<rho,k_j> to fp16 for
- * the value products, so |<rho,k_j>| must stay below 4094. */
+ * rounds the softmax numerators P (kept <= 16) and <rho,k_j> to fp16 and forms
+ * T = P*<rho,k_j> in fp16 for the value products, so |<rho,k_j>| must stay
+ * below 4094. */
 size_t parallax_prefill_workspace_bytes(int B, int H, int L, int d, int dtype);
 
 int parallax_prefill(const void* q, const void* k, const void* v, const void* rho,
@@ -165,23 +166,37 @@ int parallax_decode_default_split(int B, int H, int Lmax, int d);
  * max_q must be at least the largest n_b (it sizes the grid).  The device
  * clamps cu_q to [0, T], n_b to min(max_q, Lmax) and ctx[b] to
  * [0, Lmax - n_b], so no access leaves q or the cache.  Cache rows at or past
- * ctx[b] + n_b are never read.  PLX_BF16 only.  The workspace (at least
- * parallax_prefill_chunk_workspace_bytes(B, H, Lmax, d) bytes, or NULL to let
- * the library allocate on `stream`) holds the fp16 V^T tiles of the cache
- * rows the chunks read. */
-size_t parallax_prefill_chunk_workspace_bytes(int B, int H, int Lmax, int d);
+ * ctx[b] + n_b are never read.  PLX_BF16 only.
+ * split_keys: with fewer query tiles than the GPU has room for (few sequences,
+ * short chunks), the cache prefix of every query tile is split into ranges of
+ * split_keys keys, attended by separate workgroups into partial states that a
+ * second kernel merges per query row in a fixed order (split-KV; exact up to
+ * fp32 rounding order).  0 picks the library's split
+ * (parallax_prefill_chunk_default_split); otherwise a positive multiple of 64,
+ * where split_keys >= Lmax means no split.  Other values are PLX_EINVAL.
+ * The workspace (at least parallax_prefill_chunk_workspace_bytes(B, H, T,
+ * Lmax, max_q, d, split_keys) bytes, or NULL to let the library allocate on
+ * `stream`) holds the fp16 V^T tiles of the cache rows the chunks read and,
+ * when split, the partial states (T*H*S records of 2d+4 floats,
+ * S = ceil(ceil(Lmax/64) / (split_keys/64))). */
+size_t parallax_prefill_chunk_workspace_bytes(int B, int H, int T, int Lmax, int max_q, int d,
+                                              int split_keys);
 
 int parallax_prefill_chunk(const void* q, const void* kcache, const void* vcache,
                            const void* rho, const float* gate, float* out,
                            const int32_t* cu_q, const int32_t* ctx, int B, int H, int T,
-                           int Lmax, int max_q, int d, float scale, int dtype,
+                           int Lmax, int max_q, int d, float scale, int dtype, int split_keys,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Keys per split parallax_prefill_chunk uses for split_keys = 0: a multiple of
+ * 64, at least Lmax when it does not split (0 for invalid sizes). */
+int parallax_prefill_chunk_default_split(int B, int H, int Lmax, int max_q, int d);
 
 /* A serving loop can keep the V cache's staged copy and skip the per-call
  * staging, which for short chunks is most of the traffic: vt_cache
- * ([B, H, ceil(Lmax/64), d, 64] fp16, parallax_prefill_chunk_workspace_bytes()
- * bytes, the layout of parallax_prefill_stage_v applied to the cache) holds
- * V^T of every cache row.
+ * ([B, H, ceil(Lmax/64), d, 64] fp16, parallax_prefill_workspace_bytes(B, H,
+ * Lmax, d, PLX_BF16) bytes, the layout of parallax_prefill_stage_v applied to
+ * the cache) holds V^T of every cache row.
  * parallax_stage_v_rows: after the chunks' values are written to vcache,
  *   re-stages only the 64-row tiles that hold rows ctx[b] .. ctx[b]+n_b-1
  *   (arguments and clamping as in parallax_prefill_chunk); rows at or past
@@ -190,15 +205,23 @@ int parallax_prefill_chunk(const void* q, const void* kcache, const void* vcache
  *   whose tiles must hold rows 0 .. ctx[b]+n_b-1 of each sequence (after
  *   parallax_stage_v_rows for every append, or one parallax_prefill_stage_v of
  *   a cache whose rows are all finite).  Results are bit-identical to
- *   parallax_prefill_chunk. */
+ *   parallax_prefill_chunk with the same split_keys.  Its workspace holds only
+ *   the partial states of a split: at least
+ *   parallax_prefill_chunk_vt_workspace_bytes(B, H, T, Lmax, max_q, d,
+ *   split_keys) bytes (0 without a split), or NULL to let the library allocate
+ *   on `stream` when it needs any. */
 int parallax_stage_v_rows(const void* vcache, void* vt_cache, const int32_t* cu_q,
                           const int32_t* ctx, int B, int H, int T, int Lmax, int max_q, int d,
                           void* stream);
 
+size_t parallax_prefill_chunk_vt_workspace_bytes(int B, int H, int T, int Lmax, int max_q, int d,
+                                                 int split_keys);
+
 int parallax_prefill_chunk_vt(const void* q, const void* kcache, const void* vt_cache,
                               const void* rho, const float* gate, float* out,
                               const int32_t* cu_q, const int32_t* ctx, int B, int H, int T,
-                              int Lmax, int max_q, int d, float scale, int dtype, void* stream);
+                              int Lmax, int max_q, int d, float scale, int dtype, int split_keys,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* --------------------------------------------------------- softmax baseline
  * Plain causal softmax attention, o_i = o^SA_i (Eq. 2 without the correction

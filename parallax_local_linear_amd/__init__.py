@@ -28,7 +28,8 @@ __all__ = ["prefill", "decode", "prefill_stage_v", "prefill_attend", "decode_par
            "decode_default_split", "softmax_prefill", "softmax_prefill_attend",
            "softmax_decode", "prefill_train", "prefill_backward",
            "prefill_backward_workspace_bytes", "prefill_chunk", "stage_v_rows",
-           "chunk_vt_cache", "parallax_attention", "ParallaxAttentionFunction",
+           "chunk_vt_cache", "chunk_default_split", "parallax_attention",
+           "ParallaxAttentionFunction",
            "ParallaxError"]
 
 _DT = {torch.bfloat16: PLX_BF16, torch.float32: PLX_F32}
@@ -205,10 +206,13 @@ def _chunk_checks(q, kcache, rho, gate, cu_q, ctx):
     return T, H, d, B, Lmax
 
 
+def _vt_cache_bytes(B, H, Lmax, d):
+    return int(lib().parallax_prefill_workspace_bytes(B, H, Lmax, d, PLX_BF16))
+
+
 def chunk_vt_cache(B, H, Lmax, d, device):
     """An empty staged V^T cache for prefill_chunk(..., vt_cache=...)."""
-    n = int(lib().parallax_prefill_chunk_workspace_bytes(B, H, Lmax, d))
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.empty(_vt_cache_bytes(B, H, Lmax, d), dtype=torch.uint8, device=device)
 
 
 def stage_v_rows(vcache, vt_cache, cu_q, ctx, max_q, T):
@@ -219,8 +223,7 @@ def stage_v_rows(vcache, vt_cache, cu_q, ctx, max_q, T):
         raise ValueError("vcache must be [B, H, Lmax, d]")
     B, H, Lmax, d = vcache.shape
     _check("vt_cache", vt_cache, device=vcache.device)
-    if vt_cache.numel() * vt_cache.element_size() < int(
-            lib().parallax_prefill_chunk_workspace_bytes(B, H, Lmax, d)):
+    if vt_cache.numel() * vt_cache.element_size() < _vt_cache_bytes(B, H, Lmax, d):
         raise ValueError("vt_cache is too small")
     _check("cu_q", cu_q, torch.int32, (B + 1,), vcache.device)
     _check("ctx", ctx, torch.int32, (B,), vcache.device)
@@ -229,36 +232,49 @@ def stage_v_rows(vcache, vt_cache, cu_q, ctx, max_q, T):
     return vt_cache
 
 
+def chunk_default_split(B, H, Lmax, max_q, d):
+    """Keys per split prefill_chunk uses with split_keys=0 (>= Lmax: no split)."""
+    return int(lib().parallax_prefill_chunk_default_split(B, H, Lmax, int(max_q), d))
+
+
 def prefill_chunk(q, kcache, vcache, rho, gate, cu_q, ctx, max_q, scale=None, out=None,
-                  workspace=None, vt_cache=None):
+                  workspace=None, vt_cache=None, split_keys=0):
     """Chunked causal prefill against a KV cache (bf16).  q, rho: [T, H, d]
     packed token-major; kcache, vcache: [B, H, Lmax, d] holding each chunk's
     own keys at positions ctx[b] .. ctx[b]+n_b-1; cu_q [B+1] and ctx [B] int32 on
     the GPU; max_q >= the largest chunk.  With vt_cache (kept up to date by
     stage_v_rows) V is read from the staged cache and vcache may be None.
-    Returns out [T, H, d] fp32."""
+    split_keys: keys per split-KV range (0: the library's choice; a multiple of
+    64, >= Lmax for none).  Returns out [T, H, d] fp32."""
     T, H, d, B, Lmax = _chunk_checks(q, kcache, rho, gate, cu_q, ctx)
     if out is None:
         out = torch.empty((T, H, d), dtype=torch.float32, device=q.device)
     _check("out", out, torch.float32, (T, H, d), q.device)
+    sk, mq = int(split_keys), int(max_q)
     if vt_cache is not None:
         _check("vt_cache", vt_cache, device=q.device)
-        if vt_cache.numel() * vt_cache.element_size() < int(
-                lib().parallax_prefill_chunk_workspace_bytes(B, H, Lmax, d)):
+        if vt_cache.numel() * vt_cache.element_size() < _vt_cache_bytes(B, H, Lmax, d):
             raise ValueError("vt_cache is too small")
+        wsb = int(lib().parallax_prefill_chunk_vt_workspace_bytes(B, H, T, Lmax, mq, d, sk))
+        if workspace is None and wsb > 0:
+            workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+        if workspace is not None:
+            _check("workspace", workspace, device=q.device)
+            wsb = workspace.numel() * workspace.element_size()
         _launch(q.device, "parallax_prefill_chunk_vt", _ptr(q), _ptr(kcache), _ptr(vt_cache),
-                _ptr(rho), _ptr(gate), _ptr(out), _ptr(cu_q), _ptr(ctx), B, H, T, Lmax,
-                int(max_q), d, _scale(scale, d), PLX_BF16)
+                _ptr(rho), _ptr(gate), _ptr(out), _ptr(cu_q), _ptr(ctx), B, H, T, Lmax, mq, d,
+                _scale(scale, d), PLX_BF16, sk,
+                _ptr(workspace), wsb)
         return out
     _check("vcache", vcache, torch.bfloat16, (B, H, Lmax, d), q.device)
-    wsb = int(lib().parallax_prefill_chunk_workspace_bytes(B, H, Lmax, d))
+    wsb = int(lib().parallax_prefill_chunk_workspace_bytes(B, H, T, Lmax, mq, d, sk))
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
     _check("workspace", workspace, device=q.device)
     wsb = workspace.numel() * workspace.element_size()
     _launch(q.device, "parallax_prefill_chunk", _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(rho),
-            _ptr(gate), _ptr(out), _ptr(cu_q), _ptr(ctx), B, H, T, Lmax, int(max_q), d,
-            _scale(scale, d), PLX_BF16, _ptr(workspace), wsb)
+            _ptr(gate), _ptr(out), _ptr(cu_q), _ptr(ctx), B, H, T, Lmax, mq, d,
+            _scale(scale, d), PLX_BF16, sk, _ptr(workspace), wsb)
     return out
 
 

@@ -42,10 +42,12 @@ SIGNATURES = {
     "parallax_prefill_train": (_i, [_vp] * 9 + [_i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "parallax_prefill_backward_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "parallax_prefill_backward": (_i, [_vp] * 15 + [_i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
-    "parallax_prefill_chunk_workspace_bytes": (_sz, [_i, _i, _i, _i]),
-    "parallax_prefill_chunk": (_i, [_vp] * 8 + [_i] * 6 + [_f, _i, _vp, _sz, _vp]),
+    "parallax_prefill_chunk_workspace_bytes": (_sz, [_i] * 7),
+    "parallax_prefill_chunk": (_i, [_vp] * 8 + [_i] * 6 + [_f, _i, _i, _vp, _sz, _vp]),
+    "parallax_prefill_chunk_default_split": (_i, [_i] * 5),
+    "parallax_prefill_chunk_vt_workspace_bytes": (_sz, [_i] * 7),
     "parallax_stage_v_rows": (_i, [_vp] * 4 + [_i] * 6 + [_vp]),
-    "parallax_prefill_chunk_vt": (_i, [_vp] * 8 + [_i] * 6 + [_f, _i, _vp]),
+    "parallax_prefill_chunk_vt": (_i, [_vp] * 8 + [_i] * 6 + [_f, _i, _i, _vp, _sz, _vp]),
 }
 
 _lib = None

@@ -39,7 +39,11 @@ size_t bwd_workspace_bytes(int B, int H, int L, int d);
 hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, const void* rho,
                                 const float* gate, float* out, const int* cu_q, const int* ctx,
                                 int B, int H, int T, int Lmax, int max_q, int d, float scale,
-                                void* vt, hipStream_t s);
+                                int split_keys, void* vt, float* part, hipStream_t s);
+int chunk_default_split(int B, int H, int Lmax, int max_q, int d);
+int chunk_num_splits(int Lmax, int split_keys);
+size_t chunk_part_bytes(int T, int H, int Lmax, int d, int split_keys);
+long long chunk_split_blocks(int B, int H, int Lmax, int max_q, int d, int split_keys);
 hipError_t launch_stage_v_rows(const void* vc, void* vt, const int* cu_q, const int* ctx, int B,
                                int H, int T, int Lmax, int max_q, int d, bool new_rows_only,
                                hipStream_t s);
@@ -103,6 +107,28 @@ bool chunk_args_ok(int B, int H, int T, int Lmax, int max_q, int d, const char* 
   }
   return true;
 }
+
+// split_keys of a chunked prefill: 0 picks the library's split, else a positive
+// multiple of 64 (at least Lmax: no split).  The split launches must fit a 1-D
+// grid.
+bool chunk_split_ok(int split_keys, int B, int H, int Lmax, int max_q, int d, const char* fn,
+                    int* st, int* keys) {
+  if (split_keys < 0 || split_keys % 64 != 0) {
+    *st = fail(PLX_EINVAL, "%s: split_keys must be 0 or a positive multiple of 64 (got %d)", fn,
+               split_keys);
+    return false;
+  }
+  *keys = split_keys ? split_keys : plx::chunk_default_split(B, H, Lmax, max_q, d);
+  if (plx::chunk_num_splits(Lmax, *keys) > 1 &&
+      plx::chunk_split_blocks(B, H, Lmax, max_q, d, *keys) > 0x7fffffffLL) {
+    *st = fail(PLX_EINVAL, "%s: split_keys %d gives too many workgroups", fn, *keys);
+    return false;
+  }
+  return true;
+}
+
+// Split records follow the staged V^T in a chunk workspace, 256-byte aligned.
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // The decode grid puts the B*H streams on its second dimension.
 bool streams_ok(int B, int H, const char* fn, int* status) {
@@ -413,16 +439,32 @@ int parallax_prefill_backward(const void* q, const void* k, const void* v, const
   return ok();
 }
 
-size_t parallax_prefill_chunk_workspace_bytes(int B, int H, int Lmax, int d) {
-  if (B <= 0 || H <= 0 || Lmax <= 0 || (d != 64 && d != 128)) return 0;
-  return vt_bytes(B, H, Lmax, d);
+size_t parallax_prefill_chunk_workspace_bytes(int B, int H, int T, int Lmax, int max_q, int d,
+                                              int split_keys) {
+  if (B <= 0 || H <= 0 || T <= 0 || Lmax <= 0 || max_q <= 0 || (d != 64 && d != 128)) return 0;
+  if (split_keys < 0 || split_keys % 64 != 0) return 0;
+  const int keys = split_keys ? split_keys : plx::chunk_default_split(B, H, Lmax, max_q, d);
+  return align256(vt_bytes(B, H, Lmax, d)) + plx::chunk_part_bytes(T, H, Lmax, d, keys);
+}
+
+size_t parallax_prefill_chunk_vt_workspace_bytes(int B, int H, int T, int Lmax, int max_q, int d,
+                                                 int split_keys) {
+  if (B <= 0 || H <= 0 || T <= 0 || Lmax <= 0 || max_q <= 0 || (d != 64 && d != 128)) return 0;
+  if (split_keys < 0 || split_keys % 64 != 0) return 0;
+  const int keys = split_keys ? split_keys : plx::chunk_default_split(B, H, Lmax, max_q, d);
+  return plx::chunk_part_bytes(T, H, Lmax, d, keys);
+}
+
+int parallax_prefill_chunk_default_split(int B, int H, int Lmax, int max_q, int d) {
+  if (B <= 0 || H <= 0 || Lmax <= 0 || max_q <= 0 || (d != 64 && d != 128)) return 0;
+  return plx::chunk_default_split(B, H, Lmax, max_q, d);
 }
 
 int parallax_prefill_chunk(const void* q, const void* kcache, const void* vcache, const void* rho,
                            const float* gate, float* out, const int32_t* cu_q,
                            const int32_t* ctx, int B, int H, int T, int Lmax, int max_q, int d,
-                           float scale, int dtype, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+                           float scale, int dtype, int split_keys, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   const char* fn = "parallax_prefill_chunk";
   int st = PLX_OK;
   if (!chunk_args_ok(B, H, T, Lmax, max_q, d, fn, &st)) return st;
@@ -430,14 +472,20 @@ int parallax_prefill_chunk(const void* q, const void* kcache, const void* vcache
   if (dtype != PLX_BF16) return fail(PLX_EUNSUPPORTED, "%s: only PLX_BF16 is supported", fn);
   if (!q || !kcache || !vcache || !rho || !gate || !out || !cu_q || !ctx)
     return fail(PLX_EINVAL, "%s: null pointer", fn);
+  int keys = 0;
+  if (!chunk_split_ok(split_keys, B, H, Lmax, max_q, d, fn, &st, &keys)) return st;
   hipStream_t s = (hipStream_t)stream;
   Scratch scratch;
   void* ws = nullptr;
-  if (!get_workspace(workspace, workspace_bytes, vt_bytes(B, H, Lmax, d), s, &scratch, &ws, fn,
+  const size_t vt_off = align256(vt_bytes(B, H, Lmax, d));
+  if (!get_workspace(workspace, workspace_bytes,
+                     vt_off + plx::chunk_part_bytes(T, H, Lmax, d, keys), s, &scratch, &ws, fn,
                      &st))
     return st;
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + vt_off);
   hipError_t e = plx::launch_prefill_chunk(q, kcache, vcache, rho, gate, out, cu_q, ctx, B, H, T,
-                                           Lmax, max_q, d, eff_scale(scale, d), ws, s);
+                                           Lmax, max_q, d, eff_scale(scale, d), keys, ws, part,
+                                           s);
   if (e != hipSuccess) return launch_fail(fn, "chunk", e);
   return ok();
 }
@@ -458,7 +506,8 @@ int parallax_stage_v_rows(const void* vcache, void* vt_cache, const int32_t* cu_
 int parallax_prefill_chunk_vt(const void* q, const void* kcache, const void* vt_cache,
                               const void* rho, const float* gate, float* out,
                               const int32_t* cu_q, const int32_t* ctx, int B, int H, int T,
-                              int Lmax, int max_q, int d, float scale, int dtype, void* stream) {
+                              int Lmax, int max_q, int d, float scale, int dtype, int split_keys,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "parallax_prefill_chunk_vt";
   int st = PLX_OK;
   if (!chunk_args_ok(B, H, T, Lmax, max_q, d, fn, &st)) return st;
@@ -466,9 +515,18 @@ int parallax_prefill_chunk_vt(const void* q, const void* kcache, const void* vt_
   if (dtype != PLX_BF16) return fail(PLX_EUNSUPPORTED, "%s: only PLX_BF16 is supported", fn);
   if (!q || !kcache || !vt_cache || !rho || !gate || !out || !cu_q || !ctx)
     return fail(PLX_EINVAL, "%s: null pointer", fn);
+  int keys = 0;
+  if (!chunk_split_ok(split_keys, B, H, Lmax, max_q, d, fn, &st, &keys)) return st;
+  hipStream_t s = (hipStream_t)stream;
+  Scratch scratch;
+  void* ws = nullptr;
+  const size_t need = plx::chunk_part_bytes(T, H, Lmax, d, keys);
+  if (need > 0 && !get_workspace(workspace, workspace_bytes, need, s, &scratch, &ws, fn, &st))
+    return st;
   hipError_t e = plx::launch_prefill_chunk(q, kcache, nullptr, rho, gate, out, cu_q, ctx, B, H, T,
-                                           Lmax, max_q, d, eff_scale(scale, d),
-                                           const_cast<void*>(vt_cache), (hipStream_t)stream);
+                                           Lmax, max_q, d, eff_scale(scale, d), keys,
+                                           const_cast<void*>(vt_cache), static_cast<float*>(ws),
+                                           s);
   if (e != hipSuccess) return launch_fail(fn, "chunk", e);
   return ok();
 }

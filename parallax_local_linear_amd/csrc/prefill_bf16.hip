@@ -136,6 +136,12 @@ struct ChunkArgs {
   int max_q;    // largest chunk: the grid covers ceil(max_q / queries per workgroup)
   int n64max;   // staged V^T tiles per (b, h): ceil(Lmax / 64)
   int new_rows_only;   // staging: only the tiles that hold cache rows >= ctx[b]
+  // split-KV chunked prefill: split s of every query tile covers key tiles
+  // s*split_tiles .. (s+1)*split_tiles - 1; its partial records go to part
+  // ([T*H][n_split][2D+4] floats, row index token*H + head)
+  int split_tiles;
+  int n_split;
+  float* part;
 };
 // (first row, queries, position of query 0) of sequence b, clamped
 __device__ __forceinline__ void chunk_geometry(const ChunkArgs& ca, int b, int* c0, int* n_q,
@@ -155,8 +161,10 @@ __device__ __forceinline__ void chunk_geometry(const ChunkArgs& ca, int b, int* 
 // what the backward pass needs: the natural-log partition function of every
 // row, rbar = c / l and the correction vector (u - o_sa rbar).  VARLEN = true
 // is the chunked prefill (ChunkArgs): the same tile loop with the causal mask
-// offset by the chunk's cache position.
-template <int D, int NW, bool PIPE, bool CORR, bool SAVE, bool VARLEN>
+// offset by the chunk's cache position.  SPLIT (with VARLEN) walks only the key
+// tiles of one split and writes the unnormalised state of every row (m, l, c,
+// sum p v, sum p r v) to ca.part for chunk_combine_kernel.
+template <int D, int NW, bool PIPE, bool CORR, bool SAVE, bool VARLEN, bool SPLIT>
 __global__ __launch_bounds__(64 * NW, CORR ? (D == 64 ? PLX_PF_MINW_D64 : PLX_PF_MINW_D128)
                                           : (D == 64 ? PLX_SM_MINW_D64 : PLX_SM_MINW_D128))
 void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -167,6 +175,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
                          float sl2, ChunkArgs ca) {
   static_assert(CORR || !SAVE, "the training statistics belong to the Parallax kernel");
   static_assert(!(SAVE && VARLEN), "the training statistics are for whole sequences");
+  static_assert(!SPLIT || (VARLEN && CORR), "key splits are for the chunked prefill");
   using LY = PfLayout<D>;
   constexpr int PF_BR = 16 * NW;                         // queries per workgroup
   constexpr int PF_THREADS = 64 * NW;
@@ -181,8 +190,14 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   const int c16 = lane & 15;
   const int g4 = lane >> 4;
 
-  const int qt = n_qt - 1 - (int)(blockIdx.x / (unsigned)BH);
+  int qt = n_qt - 1 - (int)(blockIdx.x / (unsigned)BH);
   const int bh = (int)(blockIdx.x % (unsigned)BH);
+  int sp = 0;                                    // key split (SPLIT)
+  if constexpr (SPLIT) {
+    const int rest = (int)(blockIdx.x / (unsigned)BH);
+    qt = n_qt - 1 - rest % n_qt;
+    sp = rest / n_qt;
+  }
   const int h = bh % H;
   const int q0 = qt * PF_BR;
   const int qw0 = q0 + wave * 16;
@@ -197,8 +212,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   size_t qbase = head, qstride = D;
   const __bf16* kh = k + head;
   const _Float16* vth = vt + (size_t)bh * n_kt_all * (D * PF_BC);
+  int c0 = 0;
   if constexpr (VARLEN) {
-    int c0;
     chunk_geometry(ca, bh / H, &c0, &n_q, &pos0);
     if (q0 >= n_q) return;                       // uniform over the workgroup
     qbase = ((size_t)c0 * H + h) * D;
@@ -245,6 +260,15 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 
   const int last_pos = pos0 + min(q0 + PF_BR, n_q) - 1;
   const int n_kt = last_pos / PF_BC + 1;
+  // Key tiles this workgroup walks: 0 .. n_kt-1, or with SPLIT those of split
+  // sp.  A split that starts past n_kt holds no key of these queries (and no
+  // combine reads its records).
+  int t_beg = 0, t_end = n_kt;
+  if constexpr (SPLIT) {
+    t_beg = sp * ca.split_tiles;
+    if (t_beg >= n_kt) return;                   // uniform over the workgroup
+    t_end = min(n_kt, t_beg + ca.split_tiles);
+  }
   const int wave_last_pos = pos0 + min(qw0 + 15, n_q - 1);
 
   // Tiles move HBM -> LDS with buffer_load_dwordx4 ... lds: each lane's 16
@@ -319,6 +343,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // a tile needs the causal mask when its last key follows the wave's first
   // query (for a whole-sequence prefill, only the wave's last tile)
   const int n_w = (qw0 < n_q) ? wave_last_pos / PF_BC + 1 : 0;
+  const int w_end = SPLIT ? min(n_w, t_end) : n_w;   // this wave computes tiles t_beg .. w_end-1
   auto needs_mask = [&](int t) { return t * PF_BC + PF_BC - 1 > pos0 + qw0; };
 
   // K and V tiles are double-buffered.  Pipelined schedule: K runs one tile
@@ -329,9 +354,9 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   using KAll0 = std::integral_constant<int, 0>;
   using KHalf = std::integral_constant<int, KBLK / NW / 2>;
   using KAll1 = std::integral_constant<int, KBLK / NW>;
-  load_k(0, 0, KAll0{}, KAll1{});
-  load_v(0, 0);
-  if (PIPE && n_kt > 1) load_k(1, 1, KAll0{}, KAll1{});
+  load_k(t_beg, 0, KAll0{}, KAll1{});
+  load_v(t_beg, 0);
+  if (PIPE && t_end - t_beg > 1) load_k(t_beg + 1, 1, KAll0{}, KAll1{});
   wait_loads();
   __syncthreads();
 
@@ -420,17 +445,18 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     // The second half of the K tile two steps ahead and the V tile of the next
     // step are staged here rather than at the top of the iteration: the wave's
     // vector-memory issue then overlaps its score MFMAs instead of delaying them.
-    load_k(min(kt_ + 2, n_kt - 1), P, KHalf{}, KAll1{});
-    load_v(min(kt_ + 1, n_kt - 1), 1 - P);
+    load_k(min(kt_ + 2, t_end - 1), P, KHalf{}, KAll1{});
+    load_v(min(kt_ + 1, t_end - 1), 1 - P);
     softmax_pv(par, cs, cr);
     return tile_max(ns, kt_ + 1, diag_next);
   };
 
   f32x4 sn[4], rn[4];     // the other score register set of the pipelined loop
   if constexpr (PIPE) {
-    if (n_w > 0) {
+    if (w_end > t_beg) {
       scores(std::integral_constant<int, 0>{}, sc, rc);
-      m_run = needs_mask(0) ? tile_max(sc, 0, std::true_type{}) : tile_max(sc, 0, std::false_type{});
+      m_run = needs_mask(t_beg) ? tile_max(sc, t_beg, std::true_type{})
+                                : tile_max(sc, t_beg, std::false_type{});
     }
     // iteration 0 overwrites K buffer 0: every wave must be done reading it
     __syncthreads();
@@ -443,16 +469,16 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     // Staging is unconditional: past the last tile the loads re-read tile
     // n_kt-1 into buffers no wave reads again.
     const int k_ahead = PIPE ? kt + 2 : kt + 1;
-    const bool in_step = PIPE && kt + 1 < n_w;     // pipe_step stages the rest itself
+    const bool in_step = PIPE && kt + 1 < w_end;   // pipe_step stages the rest itself
     if (in_step) {
-      load_k(min(k_ahead, n_kt - 1), P, KAll0{}, KHalf{});
+      load_k(min(k_ahead, t_end - 1), P, KAll0{}, KHalf{});
     } else {
-      load_k(min(k_ahead, n_kt - 1), PIPE ? P : 1 - P, KAll0{}, KAll1{});
-      load_v(min(kt + 1, n_kt - 1), 1 - P);
+      load_k(min(k_ahead, t_end - 1), PIPE ? P : 1 - P, KAll0{}, KAll1{});
+      load_v(min(kt + 1, t_end - 1), 1 - P);
     }
-    if (kt < n_w) {
+    if (kt < w_end) {
       if constexpr (PIPE) {
-        if (kt + 1 < n_w) {
+        if (kt + 1 < w_end) {
           const float m_next =
               needs_mask(kt + 1) ? pipe_step(kt, par, std::true_type{}, cs, cr, ns, nr)
                                  : pipe_step(kt, par, std::false_type{}, cs, cr, ns, nr);
@@ -464,7 +490,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         scores(par, cs, cr);
         const float m_tile = needs_mask(kt) ? tile_max(cs, kt, std::true_type{})
                                             : tile_max(cs, kt, std::false_type{});
-        if (kt == 0) m_run = m_tile;            // accumulators are still zero
+        if (kt == t_beg) m_run = m_tile;        // accumulators are still zero
         rescale_to(m_tile);
         softmax_pv(par, cs, cr);
       }
@@ -472,14 +498,29 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     wait_loads();
     __syncthreads();
   };
-  for (int kt = 0; kt < n_kt; kt += 2) {
+  for (int kt = t_beg; kt < t_end; kt += 2) {
     iteration(kt, std::integral_constant<int, 0>{}, sc, rc, sn, rn);
-    if (kt + 1 < n_kt) iteration(kt + 1, std::integral_constant<int, 1>{}, sn, rn, sc, rc);
+    if (kt + 1 < t_end) iteration(kt + 1, std::integral_constant<int, 1>{}, sn, rn, sc, rc);
   }
 
   // epilogue: o = o_sa - g (u - o_sa * rbar), o_sa = O/l, u = A_r/l, rbar = c/l
   const float l_tot = acc_l[0];
   const float c_tot = acc_c[0];
+  if constexpr (SPLIT) {
+    // the split's unnormalised state, relative to 2^m_run; a row whose keys all
+    // precede this split leaves a record no combine reads
+    if (qi < n_q) {
+      constexpr int RF = 2 * D + 4;
+      float* rec = ca.part + (((size_t)(c0 + qi) * H + h) * ca.n_split + sp) * RF;
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        *reinterpret_cast<f32x4*>(rec + 4 + 16 * fb + 4 * g4) = acc_o[fb];
+        *reinterpret_cast<f32x4*>(rec + 4 + D + 16 * fb + 4 * g4) = acc_r[fb];
+      }
+      if (g4 == 0) *reinterpret_cast<f32x4*>(rec) = f32x4{m_run, l_tot, c_tot, 0.f};
+    }
+    return;
+  }
   if (qi < n_q) {
     const float inv = 1.0f / l_tot;
     const float rbar = c_tot * inv;
@@ -608,15 +649,17 @@ struct TrainOut {
   float* corr;
 };
 
-template <int D, int NW, bool PIPE, bool CORR, bool SAVE = false, bool VARLEN = false>
+template <int D, int NW, bool PIPE, bool CORR, bool SAVE = false, bool VARLEN = false,
+          bool SPLIT = false>
 static hipError_t launch_prefill_t(const void* q, const void* k, const void* vt,
                                    const void* rho, const float* gate, float* out, int B,
                                    int H, int L, float sl2, hipStream_t s, TrainOut tr = {},
                                    ChunkArgs ca = {}) {
   const int BH = B * H;
   const int n_qt = ((VARLEN ? ca.max_q : L) + 16 * NW - 1) / (16 * NW);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, PIPE, CORR, SAVE, VARLEN>),
-                     dim3((unsigned)(BH * n_qt)), dim3(64 * NW), 0, s, (const __bf16*)q,
+  const unsigned n_blocks = (unsigned)BH * (unsigned)n_qt * (SPLIT ? (unsigned)ca.n_split : 1u);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, PIPE, CORR, SAVE, VARLEN, SPLIT>),
+                     dim3(n_blocks), dim3(64 * NW), 0, s, (const __bf16*)q,
                      (const __bf16*)k, (const _Float16*)vt, (const __bf16*)rho, gate, out, tr.lse,
                      tr.rbar, tr.corr, H, L, BH, n_qt, sl2, ca);
   return hipGetLastError();
@@ -661,18 +704,130 @@ hipError_t launch_stage_v_rows(const void* vc, void* vt, const int* cu_q, const 
   return hipGetLastError();
 }
 
+// Merge the split records of every chunk row over the splits that start at or
+// before the row's cache position (each holds at least one of its keys; later
+// splits hold none) and write o = o_sa - g (u - o_sa rbar).  One workgroup of D
+// threads per (chunk query j, head b*H + h), heads fastest; the merge order is
+// fixed.
+template <int D>
+__global__ __launch_bounds__(D)
+void chunk_combine_kernel(const float* __restrict__ gate, float* __restrict__ out, int H, int BH,
+                          ChunkArgs ca) {
+  const int j = (int)(blockIdx.x / (unsigned)BH);
+  const int bh = (int)(blockIdx.x % (unsigned)BH);
+  const int b = bh / H, h = bh % H;
+  int c0, n_q, pos0;
+  chunk_geometry(ca, b, &c0, &n_q, &pos0);
+  if (j >= n_q) return;
+  const int f = threadIdx.x;
+  constexpr int RF = 2 * D + 4;
+  const int ns = (pos0 + j) / (ca.split_tiles * PF_BC) + 1;
+  const size_t row = (size_t)(c0 + j) * H + h;
+  const float* rec = ca.part + row * ca.n_split * RF;
+  float M = kMinit;
+  for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, rec[(size_t)sp * RF]);
+  float l = 0.f, c = 0.f, a = 0.f, bv = 0.f;
+  for (int sp = 0; sp < ns; ++sp) {
+    const float* r = rec + (size_t)sp * RF;
+    const float w = __builtin_amdgcn_exp2f(r[0] - M);
+    l += w * r[1];
+    c += w * r[2];
+    a += w * r[4 + f];
+    bv += w * r[4 + D + f];
+  }
+  const float inv = 1.0f / l;
+  const float osa = a * inv;
+  out[row * D + f] = osa - gate[h] * (bv * inv - osa * (c * inv));
+}
+
+// Keys per split the chunked prefill uses by default: none (one split of the
+// whole cache) once the query tiles alone give PLX_CHUNK_SPLIT_BELOW
+// workgroups (one per CU), else enough splits for PLX_CHUNK_SPLIT_TARGET
+// workgroups, each at least PLX_CHUNK_SPLIT_MIN_TILES tiles long.  Measured:
+// splitting 256 - 384 query tiles (one or two workgroups per CU already) costs
+// 4 - 9 % in record traffic; below 256 it gains up to 8x.
+#ifndef PLX_CHUNK_SPLIT_BELOW
+#define PLX_CHUNK_SPLIT_BELOW 256
+#endif
+#ifndef PLX_CHUNK_SPLIT_TARGET
+#define PLX_CHUNK_SPLIT_TARGET 512
+#endif
+#ifndef PLX_CHUNK_SPLIT_MIN_TILES
+#define PLX_CHUNK_SPLIT_MIN_TILES 4
+#endif
+constexpr int kChunkMinSplitTiles = PLX_CHUNK_SPLIT_MIN_TILES;
+constexpr int kChunkTargetBlocks = PLX_CHUNK_SPLIT_TARGET;
+int chunk_default_split(int B, int H, int Lmax, int max_q, int d) {
+  const int qpb = 16 * (d == 128 ? PLX_PF_NW_D128 : PLX_PF_NW_D64);
+  const int n64 = (Lmax + PF_BC - 1) / PF_BC;
+  const long long base = (long long)B * H * ((min(max_q, Lmax) + qpb - 1) / qpb);
+  if (base <= 0 || base >= PLX_CHUNK_SPLIT_BELOW) return n64 * PF_BC;
+  const int want = (int)((kChunkTargetBlocks + base - 1) / base);
+  const int tiles = max(kChunkMinSplitTiles, (n64 + want - 1) / want);
+  return min(tiles, n64) * PF_BC;
+}
+
+// Splits of split_keys keys over a cache of Lmax rows (1: no split).
+int chunk_num_splits(int Lmax, int split_keys) {
+  const int n64 = (Lmax + PF_BC - 1) / PF_BC;
+  const int st = split_keys / PF_BC;
+  return (n64 + st - 1) / st;
+}
+
+// Workgroups of the larger of the two split-KV launches (the API keeps it
+// within a 1-D grid).
+long long chunk_split_blocks(int B, int H, int Lmax, int max_q, int d, int split_keys) {
+  const int qpb = 16 * (d == 128 ? PLX_PF_NW_D128 : PLX_PF_NW_D64);
+  const long long mq = min(max_q, Lmax);
+  const long long attend = (long long)B * H * ((mq + qpb - 1) / qpb) *
+                           chunk_num_splits(Lmax, split_keys);
+  const long long combine = (long long)B * H * mq;
+  return attend > combine ? attend : combine;
+}
+
+// Bytes of split records a chunked prefill over T query rows needs (0 without
+// a split).
+size_t chunk_part_bytes(int T, int H, int Lmax, int d, int split_keys) {
+  const int ns = chunk_num_splits(Lmax, split_keys);
+  return ns > 1 ? (size_t)T * H * ns * (2 * d + 4) * sizeof(float) : 0;
+}
+
 // Chunked prefill: unless the caller keeps the V cache staged (vc == null),
-// stage V^T of the cache rows each chunk reads into vt; then attend.
+// stage V^T of the cache rows each chunk reads into vt; then attend, over the
+// whole cache prefix or, with more than one split of split_keys keys (a
+// multiple of 64), split by split into part and then combined.
 hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, const void* rho,
                                 const float* gate, float* out, const int* cu_q, const int* ctx,
                                 int B, int H, int T, int Lmax, int max_q, int d, float scale,
-                                void* vt, hipStream_t s) {
+                                int split_keys, void* vt, float* part, hipStream_t s) {
   const float sl2 = scale * kLog2e;
   const int n64 = (Lmax + PF_BC - 1) / PF_BC;
-  const ChunkArgs ca{cu_q, ctx, T, Lmax, max_q, n64, 0};
+  ChunkArgs ca{cu_q, ctx, T, Lmax, max_q, n64, 0};
   if (vc) {
     hipError_t e = launch_stage_v_rows(vc, vt, cu_q, ctx, B, H, T, Lmax, max_q, d, false, s);
     if (e != hipSuccess) return e;
+  }
+  const int n_split = chunk_num_splits(Lmax, split_keys);
+  if (n_split > 1) {
+    ca.split_tiles = split_keys / PF_BC;
+    ca.n_split = n_split;
+    ca.part = part;
+    hipError_t e;
+    if (d == 128)
+      e = launch_prefill_t<128, PLX_PF_NW_D128, (PLX_PF_PIPE_D128 != 0), true, false, true, true>(
+          q, kc, vt, rho, gate, out, B, H, Lmax, sl2, s, {}, ca);
+    else
+      e = launch_prefill_t<64, PLX_PF_NW_D64, (PLX_PF_PIPE_D64 != 0), true, false, true, true>(
+          q, kc, vt, rho, gate, out, B, H, Lmax, sl2, s, {}, ca);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)min(max_q, Lmax) * (unsigned)(B * H));
+    if (d == 128)
+      hipLaunchKernelGGL((chunk_combine_kernel<128>), grid, dim3(128), 0, s, gate, out, H, B * H,
+                         ca);
+    else
+      hipLaunchKernelGGL((chunk_combine_kernel<64>), grid, dim3(64), 0, s, gate, out, H, B * H,
+                         ca);
+    return hipGetLastError();
   }
   if (d == 128)
     return launch_prefill_t<128, PLX_PF_NW_D128, (PLX_PF_PIPE_D128 != 0), true, false, true>(

@@ -192,36 +192,68 @@ void training_and_chunk_rejections() {
                                    PLX_BF16, P(15), bw - 1, nullptr), PLX_EINVAL, fb,
          "backward workspace too small");
   const char* fc = "parallax_prefill_chunk";
-  check(parallax_prefill_chunk_workspace_bytes(2, 3, 130, 128) ==
-            parallax_prefill_workspace_bytes(2, 3, 130, 128, PLX_BF16),
-        "chunk workspace = V^T tiles of the cache");
+  // 1 x 3 heads, 16-query chunks, 130 cache rows: no split when the split
+  // covers the cache, else 3 splits of 64 keys for 8 query rows
+  check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 16, 128, 192) ==
+            ((parallax_prefill_workspace_bytes(2, 3, 130, 128, PLX_BF16) + 255) & ~(size_t)255),
+        "chunk workspace = V^T tiles of the cache without a split");
+  check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 16, 128, 64) ==
+            ((parallax_prefill_workspace_bytes(2, 3, 130, 128, PLX_BF16) + 255) & ~(size_t)255) +
+                (size_t)8 * 3 * 3 * (2 * 128 + 4) * 4,
+        "chunk workspace adds T*H*S records of 2d+4 floats");
+  check(parallax_prefill_chunk_vt_workspace_bytes(2, 3, 8, 130, 16, 128, 192) == 0,
+        "chunk_vt workspace without a split");
+  check(parallax_prefill_chunk_vt_workspace_bytes(2, 3, 8, 130, 16, 128, 64) ==
+            (size_t)8 * 3 * 3 * (2 * 128 + 4) * 4,
+        "chunk_vt workspace = the split records");
+  check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 16, 128, 100) == 0,
+        "chunk workspace of a bad split size");
+  // default split: one 16-query tile per head wants 512 workgroups, at least 4
+  // tiles per split; 512 query tiles already fill the GPU
+  check(parallax_prefill_chunk_default_split(1, 1, 8192, 16, 128) == 256, "default split, B*H=1");
+  check(parallax_prefill_chunk_default_split(2, 16, 8192, 16, 128) == 512,
+        "default split, B*H=32");
+  check(parallax_prefill_chunk_default_split(32, 16, 8192, 16, 128) >= 8192,
+        "no split for 512 query tiles");
+  check(parallax_prefill_chunk_default_split(1, 1, 200, 16, 64) >= 200,
+        "no split below 4 tiles of cache");
+  check(parallax_prefill_chunk_default_split(0, 1, 200, 16, 64) == 0, "default split, B=0");
   expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 0, 64, 8, 64,
-                                0.f, PLX_BF16, nullptr, 0, nullptr), PLX_EINVAL, fc, "chunk T=0");
+                                0.f, PLX_BF16, 0, nullptr, 0, nullptr), PLX_EINVAL, fc, "chunk T=0");
   expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 0, 64,
-                                0.f, PLX_BF16, nullptr, 0, nullptr), PLX_EINVAL, fc,
+                                0.f, PLX_BF16, 0, nullptr, 0, nullptr), PLX_EINVAL, fc,
          "chunk max_q=0");
   expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), nullptr, I(7), 1, 1, 8, 64, 8,
-                                64, 0.f, PLX_BF16, nullptr, 0, nullptr), PLX_EINVAL, fc,
+                                64, 0.f, PLX_BF16, 0, nullptr, 0, nullptr), PLX_EINVAL, fc,
          "chunk null cu_q");
   expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8, 80,
-                                0.f, PLX_BF16, nullptr, 0, nullptr), PLX_EUNSUPPORTED, fc,
+                                0.f, PLX_BF16, 0, nullptr, 0, nullptr), PLX_EUNSUPPORTED, fc,
          "chunk d=80");
   expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8, 64,
-                                0.f, PLX_F32, nullptr, 0, nullptr), PLX_EUNSUPPORTED, fc,
+                                0.f, PLX_F32, 0, nullptr, 0, nullptr), PLX_EUNSUPPORTED, fc,
          "chunk fp32");
   expect(parallax_stage_v_rows(nullptr, P(1), I(2), I(3), 1, 1, 8, 64, 8, 64, nullptr), PLX_EINVAL,
          "parallax_stage_v_rows", "stage rows null vcache");
   expect(parallax_stage_v_rows(P(0), P(1), I(2), I(3), 1, 1, 0, 64, 8, 64, nullptr), PLX_EINVAL,
          "parallax_stage_v_rows", "stage rows T=0");
   expect(parallax_prefill_chunk_vt(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8,
-                                   64, 0.f, PLX_F32, nullptr), PLX_EUNSUPPORTED,
+                                   64, 0.f, PLX_F32, 0, nullptr, 0, nullptr), PLX_EUNSUPPORTED,
          "parallax_prefill_chunk_vt", "chunk_vt fp32");
   expect(parallax_prefill_chunk_vt(P(0), P(1), nullptr, P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64,
-                                   8, 64, 0.f, PLX_BF16, nullptr), PLX_EINVAL,
+                                   8, 64, 0.f, PLX_BF16, 0, nullptr, 0, nullptr), PLX_EINVAL,
          "parallax_prefill_chunk_vt", "chunk_vt null vt_cache");
-  const size_t cw = parallax_prefill_chunk_workspace_bytes(2, 2, 300, 64);
+  expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8, 64,
+                                0.f, PLX_BF16, -64, nullptr, 0, nullptr), PLX_EINVAL, fc,
+         "chunk negative split");
+  expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8, 64,
+                                0.f, PLX_BF16, 96, nullptr, 0, nullptr), PLX_EINVAL, fc,
+         "chunk split not a multiple of 64");
+  expect(parallax_prefill_chunk_vt(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 640, 8,
+                                   64, 0.f, PLX_BF16, 64, P(8), 1, nullptr), PLX_EINVAL,
+         "parallax_prefill_chunk_vt", "chunk_vt split workspace too small");
+  const size_t cw = parallax_prefill_chunk_workspace_bytes(2, 2, 40, 300, 20, 64, 0);
   expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 2, 2, 40, 300, 20,
-                                64, 0.f, PLX_BF16, P(8), cw - 1, nullptr), PLX_EINVAL, fc,
+                                64, 0.f, PLX_BF16, 0, P(8), cw - 1, nullptr), PLX_EINVAL, fc,
          "chunk workspace too small");
 }
 
@@ -283,18 +315,21 @@ void no_device_failures() {
                                    F(10), F(11), F(12), F(13), F(14), 1, 1, 64, 64, 0.f,
                                    PLX_BF16, nullptr, 0, nullptr), PLX_ENOMEM,
          "parallax_prefill_backward", "backward allocation failure");
-  const size_t cws = parallax_prefill_chunk_workspace_bytes(1, 1, 64, 64);
+  const size_t cws = parallax_prefill_chunk_workspace_bytes(1, 1, 8, 64, 8, 64, 0);
   expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8, 64,
-                                0.f, PLX_BF16, P(8), cws, nullptr), PLX_EHIP,
+                                0.f, PLX_BF16, 0, P(8), cws, nullptr), PLX_EHIP,
          "parallax_prefill_chunk", "chunk launch failure");
   expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8, 64,
-                                0.f, PLX_BF16, nullptr, 0, nullptr), PLX_ENOMEM,
+                                0.f, PLX_BF16, 0, nullptr, 0, nullptr), PLX_ENOMEM,
          "parallax_prefill_chunk", "chunk allocation failure");
   expect(parallax_stage_v_rows(P(0), P(1), I(2), I(3), 1, 1, 8, 64, 8, 64, nullptr), PLX_EHIP,
          "parallax_stage_v_rows", "stage rows launch failure");
   expect(parallax_prefill_chunk_vt(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8,
-                                   64, 0.f, PLX_BF16, nullptr), PLX_EHIP,
+                                   64, 0.f, PLX_BF16, 0, nullptr, 0, nullptr), PLX_EHIP,
          "parallax_prefill_chunk_vt", "chunk_vt launch failure");
+  expect(parallax_prefill_chunk_vt(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 640, 8,
+                                   64, 0.f, PLX_BF16, 64, nullptr, 0, nullptr), PLX_ENOMEM,
+         "parallax_prefill_chunk_vt", "chunk_vt split allocation failure");
 }
 
 void error_text_is_per_thread() {

@@ -121,15 +121,19 @@ def test_training_and_chunk_calls_reject_bad_arguments(lib):
     assert b(*([x] * 15), 1, 1, 64, 128, 0.0, 0, NULL, 0, NULL) == PLX_EUNSUPPORTED
     assert lib.parallax_prefill_backward_workspace_bytes(1, 1, 64, 128) > 0
     c = lib.parallax_prefill_chunk
-    assert c(*([x] * 8), 1, 1, 0, 64, 8, 128, 0.0, 1, NULL, 0, NULL) == PLX_EINVAL
-    assert c(*([x] * 8), 1, 1, 8, 64, 8, 48, 0.0, 1, NULL, 0, NULL) == PLX_EUNSUPPORTED
-    assert c(*([x] * 6), NULL, x, 1, 1, 8, 64, 8, 128, 0.0, 1, NULL, 0, NULL) == PLX_EINVAL
+    assert c(*([x] * 8), 1, 1, 0, 64, 8, 128, 0.0, 1, 0, NULL, 0, NULL) == PLX_EINVAL
+    assert c(*([x] * 8), 1, 1, 8, 64, 8, 48, 0.0, 1, 0, NULL, 0, NULL) == PLX_EUNSUPPORTED
+    assert c(*([x] * 6), NULL, x, 1, 1, 8, 64, 8, 128, 0.0, 1, 0, NULL, 0, NULL) == PLX_EINVAL
+    assert c(*([x] * 8), 1, 1, 8, 64, 8, 128, 0.0, 1, 32, NULL, 0, NULL) == PLX_EINVAL
+    assert lib.parallax_prefill_chunk_default_split(1, 4, 4096, 16, 128) == 256
+    assert lib.parallax_prefill_chunk_vt_workspace_bytes(1, 4, 8, 4096, 16, 128, 0) == \
+        8 * 4 * 16 * (2 * 128 + 4) * 4
     sr = lib.parallax_stage_v_rows
     assert sr(x, NULL, x, x, 1, 1, 8, 64, 8, 128, NULL) == PLX_EINVAL
     assert sr(x, x, x, x, 1, 1, 8, 64, 8, 96, NULL) == PLX_EUNSUPPORTED
     cv = lib.parallax_prefill_chunk_vt
-    assert cv(*([x] * 8), 1, 1, 8, 64, 0, 128, 0.0, 1, NULL) == PLX_EINVAL
-    assert cv(*([x] * 8), 1, 1, 8, 64, 8, 128, 0.0, 0, NULL) == PLX_EUNSUPPORTED
+    assert cv(*([x] * 8), 1, 1, 8, 64, 0, 128, 0.0, 1, 0, NULL, 0, NULL) == PLX_EINVAL
+    assert cv(*([x] * 8), 1, 1, 8, 64, 8, 128, 0.0, 0, 0, NULL, 0, NULL) == PLX_EUNSUPPORTED
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):

@@ -198,7 +198,10 @@ def test_training_writes_stay_in_bounds(d):
     _unchanged(inp, snap)
 
 
-def test_chunk_writes_stay_in_bounds():
+@pytest.mark.parametrize("split", [0, 64])
+def test_chunk_writes_stay_in_bounds(split):
+    """Per-call staging and the staged-cache call, whole-prefix (split 0 is no
+    split at this size) and split-KV (4 splits of 64 keys)."""
     lib = _native.lib()
     stream = torch.cuda.current_stream().cuda_stream
     ctx, n, H, d = [70, 0, 5], [20, 90, 1], 2, 128
@@ -206,18 +209,34 @@ def test_chunk_writes_stay_in_bounds():
     snap = _snapshot(inp)
     T = inp["T"]
     ob, op = _guarded(T * H * d * 4)
-    ws = lib.parallax_prefill_chunk_workspace_bytes(3, H, 200, d)
+    ws = lib.parallax_prefill_chunk_workspace_bytes(3, H, T, 200, inp["max_q"], d, split)
     wb, wp = _guarded(ws)
     st = lib.parallax_prefill_chunk(inp["q"].data_ptr(), inp["kcache"].data_ptr(),
                                     inp["vcache"].data_ptr(), inp["rho"].data_ptr(),
                                     inp["gate"].data_ptr(), op, inp["cu_q"].data_ptr(),
                                     inp["ctx"].data_ptr(), 3, H, T, 200, inp["max_q"], d, 0.0,
-                                    _native.PLX_BF16, wp, ws, stream)
+                                    _native.PLX_BF16, split, wp, ws, stream)
     assert st == 0, lib.parallax_last_error()
     torch.cuda.synchronize()
     _check_guards(ob, T * H * d * 4, "chunk out")
-    # only the V^T tiles of cache rows the chunks read are staged
+    # only the V^T tiles of cache rows the chunks read are staged, and a split
+    # writes only the records of splits that reach a row
     _check_guards(wb, ws, "chunk workspace", fully_written=False)
+    import parallax_local_linear_amd as plx
+    vt = plx.prefill_stage_v(inp["vcache"])
+    ob2, op2 = _guarded(T * H * d * 4)
+    rws = lib.parallax_prefill_chunk_vt_workspace_bytes(3, H, T, 200, inp["max_q"], d, split)
+    assert (rws > 0) == (split == 64)
+    rb, rp = _guarded(max(rws, 256))
+    st = lib.parallax_prefill_chunk_vt(inp["q"].data_ptr(), inp["kcache"].data_ptr(),
+                                       vt.data_ptr(), inp["rho"].data_ptr(),
+                                       inp["gate"].data_ptr(), op2, inp["cu_q"].data_ptr(),
+                                       inp["ctx"].data_ptr(), 3, H, T, 200, inp["max_q"], d, 0.0,
+                                       _native.PLX_BF16, split, rp, max(rws, 256), stream)
+    assert st == 0, lib.parallax_last_error()
+    torch.cuda.synchronize()
+    _check_guards(ob2, T * H * d * 4, "chunk_vt out")
+    _check_guards(rb, max(rws, 256), "chunk_vt records", fully_written=False)
     _unchanged(inp, snap)
 
 

@@ -1,6 +1,6 @@
 """GPU parity of the chunked prefill against a KV cache (parallax_prefill_chunk)
-with the fp64 CPU oracle (prefill_chunk).  Tolerance: 2e-2 max-abs, the bf16
-forward's bound."""
+with the fp64 CPU oracle (prefill_chunk), whole-prefix and split-KV.
+Tolerance: 2e-2 max-abs, the bf16 forward's bound."""
 import numpy as np
 import pytest
 import torch
@@ -18,9 +18,10 @@ def _plx():
     return plx
 
 
-def _run(inp, out=None):
+def _run(inp, out=None, split_keys=0):
     out = _plx().prefill_chunk(inp["q"], inp["kcache"], inp["vcache"], inp["rho"], inp["gate"],
-                               inp["cu_q"], inp["ctx"], inp["max_q"], out=out)
+                               inp["cu_q"], inp["ctx"], inp["max_q"], out=out,
+                               split_keys=split_keys)
     torch.cuda.synchronize()
     return out
 
@@ -58,12 +59,12 @@ def test_chunk_cases(case, d):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_empty_cache_chunk_is_the_prefill(d):
-    """ctx = 0 and one sequence: bit-identical to the whole-sequence prefill
-    (the same kernel arithmetic over the same tiles)."""
+    """ctx = 0 and one sequence, not split: bit-identical to the whole-sequence
+    prefill (the same kernel arithmetic over the same tiles)."""
     plx = _plx()
     L, H = 333, 2
     inp = wl.chunk_inputs(H, d, [0], [L], seed=1300 + d, device="cuda", rho_std=0.5)
-    out = _run(inp)
+    out = _run(inp, split_keys=384)
     q = inp["q"].transpose(0, 1).unsqueeze(0).contiguous()
     rho = inp["rho"].transpose(0, 1).unsqueeze(0).contiguous()
     ref = plx.prefill(q, inp["kcache"], inp["vcache"], rho, inp["gate"])
@@ -179,3 +180,58 @@ def test_incremental_serving_with_a_staged_cache(d):
         print(f"serving d{d} ctx{ctx} n{n}: max-abs {err:.3e}", flush=True)
         assert err <= TOL
         ctx = [c + m for c, m in zip(ctx, n)]
+
+
+SPLIT_CASES = [  # (ctx per sequence, chunk length per sequence, keys per split)
+    ([0], [65], 64),                                   # a split boundary inside the chunk
+    ([63, 64, 65], [1, 2, 3], 64),
+    ([60, 4, 0, 130], [16, 17, 15, 64], 64),
+    ([1000, 7], [65, 200], 128),
+    ([100, 0, 33, 257, 5], [33, 1, 128, 9, 300], 192),
+    ([3000], [16], 0),                                 # the library's split
+    ([5000, 20], [1, 130], 0),
+]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "ctx" + "-".join(map(str, c[0])) +
+                         "_n" + "-".join(map(str, c[1])) + f"_s{c[2]}")
+def test_chunk_split_kv(case, d):
+    """Split-KV: every row against the oracle, the staged-cache call with the
+    same split bit for bit, and the unsplit call within the tolerance."""
+    plx = _plx()
+    ctx, n, split = case
+    H = 3
+    inp = wl.chunk_inputs(H, d, ctx, n, seed=1600 + sum(ctx) + sum(n) + d, device="cuda",
+                          rho_std=0.5)
+    B, Lmax = len(ctx), inp["kcache"].shape[2]
+    if split == 0:
+        assert plx.chunk_default_split(B, H, Lmax, inp["max_q"], d) < Lmax   # it does split
+    out = _run(inp, split_keys=split)
+    err = float(np.max(np.abs(out.cpu().double().numpy() - _oracle(inp))))
+    print(f"split d{d} ctx{ctx} n{n} split {split}: max-abs {err:.3e}", flush=True)
+    assert err <= TOL
+    vt = plx.prefill_stage_v(inp["vcache"])
+    staged = plx.prefill_chunk(inp["q"], inp["kcache"], None, inp["rho"], inp["gate"],
+                               inp["cu_q"], inp["ctx"], inp["max_q"], vt_cache=vt,
+                               split_keys=split)
+    whole = _run(inp, split_keys=(Lmax + 63) // 64 * 64)
+    torch.cuda.synchronize()
+    assert torch.equal(staged, out)
+    assert float((whole - out).abs().max()) <= TOL
+
+
+def test_split_kv_small_batch_long_cache_sampled():
+    """Two sequences of 16-query chunks on 8192 cached keys (d=128, 16 heads):
+    the default splits each prefix into 15 ranges of 576 keys; sampled rows
+    against the oracle."""
+    plx = _plx()
+    B, H, d, ctx, n = 2, 16, 128, 8192, 16
+    inp = wl.chunk_inputs(H, d, [ctx] * B, [n] * B, seed=1700, device="cuda")
+    assert plx.chunk_default_split(B, H, ctx + n, n, d) == 576
+    out = _run(inp)
+    rows = [0, 7, 15, 16, 23, 31]
+    ref = _oracle(inp, rows=rows)
+    err = float(np.max(np.abs(out.cpu().double().numpy()[rows] - ref[rows])))
+    print(f"split B{B} H{H} ctx{ctx}: max-abs {err:.3e}", flush=True)
+    assert err <= TOL

@@ -214,6 +214,7 @@ def decode_bytes(seqlens, H, d, elem=2) -> float:
 CHUNK_WORKLOADS = {
     "chunk_bf16_B8_H16_ctx4096_q512_d128": dict(B=8, H=16, d=128, ctx=4096, n=512, seed=1101),
     "chunk_bf16_B32_H16_ctx8192_q16_d128": dict(B=32, H=16, d=128, ctx=8192, n=16, seed=1102),
+    "chunk_bf16_B2_H16_ctx8192_q16_d128": dict(B=2, H=16, d=128, ctx=8192, n=16, seed=1103),
 }
 
 
