@@ -724,9 +724,13 @@ void chunk_combine_kernel(const float* __restrict__ gate, float* __restrict__ ou
   const int ns = (pos0 + j) / (ca.split_tiles * PF_BC) + 1;
   const size_t row = (size_t)(c0 + j) * H + h;
   const float* rec = ca.part + row * ca.n_split * RF;
+  // unrolled so that several records' loads are in flight at once (the sums
+  // keep their order)
   float M = kMinit;
+#pragma unroll 8
   for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, rec[(size_t)sp * RF]);
   float l = 0.f, c = 0.f, a = 0.f, bv = 0.f;
+#pragma unroll 8
   for (int sp = 0; sp < ns; ++sp) {
     const float* r = rec + (size_t)sp * RF;
     const float w = __builtin_amdgcn_exp2f(r[0] - M);
