@@ -43,6 +43,17 @@ constexpr int BW_T = 64;    // rows per staged transposed tile (the forward's ti
 constexpr int BW_BQ = 32;   // queries per step of the key-stationary kernel
 
 // Launch shapes (waves per workgroup, 16-key blocks per wave), per head dimension.
+// Grid order of the dK/dV and dQ kernels, per head dimension: 0 = the tiles of
+// all heads in order of work with heads fastest; G > 0 = the same within groups
+// of G heads, group after group (more tiles of fewer heads share each XCD's L2).
+// Measured against 0 (bit-identical results): G = 32 at d = 128, -3.2 % on
+// B4 H16 L4096; G = 16 at d = 64, -6.7 % on B2 H32 L16384.
+#ifndef PLX_BW_HEAD_GROUP_D128
+#define PLX_BW_HEAD_GROUP_D128 32
+#endif
+#ifndef PLX_BW_HEAD_GROUP_D64
+#define PLX_BW_HEAD_GROUP_D64 16
+#endif
 #ifndef PLX_BW_KV_NW_D128
 #define PLX_BW_KV_NW_D128 8
 #endif
@@ -201,6 +212,22 @@ __device__ __forceinline__ BwdElt bwd_elt(bool keep, float s, float r, float dl,
 }
 
 // ------------------------------------------------------- key-stationary dK, dV
+// Block b of a BH * n_t grid -> (tile rank t, head bh) in the grid order above.
+template <int G>
+__device__ __forceinline__ void bwd_grid_order(int b, int BH, int n_t, int* t, int* bh) {
+  if constexpr (G > 0) {
+    const int full = BH / G;
+    const int g = b / (G * n_t);
+    const int gs = g < full ? G : BH - full * G;
+    const int r = b - g * G * n_t;
+    *t = r / gs;
+    *bh = g * G + r % gs;
+  } else {
+    *t = b / BH;
+    *bh = b % BH;
+  }
+}
+
 template <int D, int NW, int KB>
 __global__ __launch_bounds__(64 * NW, 1)
 void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -225,8 +252,9 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int wave = tid >> 6;
   const int c16 = lane & 15;
   const int g4 = lane >> 4;
-  const int kblk = (int)(blockIdx.x / (unsigned)BH);   // lowest key blocks (most work) first
-  const int bh = (int)(blockIdx.x % (unsigned)BH);
+  int kblk, bh;                                         // lowest key blocks (most work) first
+  bwd_grid_order<D == 64 ? PLX_BW_HEAD_GROUP_D64 : PLX_BW_HEAD_GROUP_D128>(
+      (int)blockIdx.x, BH, n_kblk, &kblk, &bh);
   const int h = bh % H;
   const int k0 = kblk * BK;
   const int kw0 = k0 + 16 * KB * wave;
@@ -444,8 +472,10 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int wave = tid >> 6;
   const int c16 = lane & 15;
   const int g4 = lane >> 4;
-  const int qt = n_qt - 1 - (int)(blockIdx.x / (unsigned)BH);   // longest rows first
-  const int bh = (int)(blockIdx.x % (unsigned)BH);
+  int qt, bh;                                           // longest rows first
+  bwd_grid_order<D == 64 ? PLX_BW_HEAD_GROUP_D64 : PLX_BW_HEAD_GROUP_D128>(
+      (int)blockIdx.x, BH, n_qt, &qt, &bh);
+  qt = n_qt - 1 - qt;
   const int h = bh % H;
   const int q0 = qt * BR;
   const int qw0 = q0 + wave * 16;
