@@ -176,3 +176,22 @@ def test_autograd_function_matches_the_oracle():
         g = leaves[n].grad
         assert g is not None and g.dtype == leaves[n].dtype, n
         assert _rel_err(_np(g), ref[key]) <= 2e-2, n
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_partial_head_group(d):
+    """The backward kernels run heads in groups (32 at d=128, 16 at d=64):
+    B*H = 40 leaves a partial last group at both sizes."""
+    B, H, L = 2, 20, 96
+    inp = wl.prefill_inputs(B, H, L, d, "bf16", seed=995 + d, device="cuda", rho_std=0.5,
+                            gate=("uniform", 0.2, 1.0))
+    dout = _dout((B, H, L, d), 996 + d)
+    _, grads = _run(inp, dout)
+    h = {n: inp[n].cpu() for n in inp}
+    ref = po.prefill_backward(h["q"], h["k"], h["v"], h["rho"], h["gate"], dout.cpu())
+    errs = {n: _rel_err(_np(t), ref[n]) for n, t in zip(GRADS, grads[:4])}
+    errs["dgate"] = _rel_err(_np(grads[4]), ref["dgate"])
+    print(f"backward partial group d{d}: " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()),
+          flush=True)
+    for n, e in errs.items():
+        assert e <= 2e-2, n

@@ -216,3 +216,21 @@ def test_many_heads():
         worst = max(worst, _maxerr(_host(out[b, hh]).double().numpy(), ref))
     print(f"prefill B*H=4096: max-abs {worst:.3e}", flush=True)
     assert worst <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("B,H", [(1, 20), (2, 17)])
+def test_partial_head_group_d64(B, H):
+    """d=64 runs heads in groups of 16: B*H = 20 and 34 leave a partial last
+    group, whose query tiles must all be computed (every row against the
+    oracle)."""
+    import parallax_local_linear_amd as plx
+    L, d = 200, 64
+    inp = wl.prefill_inputs(B, H, L, d, "bf16", seed=880 + B * H, device="cuda", rho_std=0.5,
+                            gate=("uniform", 0.2, 1.0))
+    out = plx.prefill(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"])
+    torch.cuda.synchronize()
+    h = {n: inp[n].cpu() for n in inp}
+    ref = po.prefill(h["q"], h["k"], h["v"], h["rho"], h["gate"])
+    err = float(np.max(np.abs(out.cpu().double().numpy() - ref)))
+    print(f"partial head group B{B} H{H}: max-abs {err:.3e}", flush=True)
+    assert err <= 2e-2
