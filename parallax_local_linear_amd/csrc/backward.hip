@@ -39,7 +39,7 @@
 
 namespace plx {
 
-constexpr int BW_T = 64;    // rows per staged transposed tile (the forward's tile)
+constexpr int BW_T = 64;    // keys per tile of the query-stationary kernel (the forward's tile)
 constexpr int BW_BQ = 32;   // queries per step of the key-stationary kernel
 
 // Launch shapes (waves per workgroup, 16-key blocks per wave), per head dimension.
@@ -73,27 +73,64 @@ constexpr int BW_BQ = 32;   // queries per step of the key-stationary kernel
 #define PLX_BW_Q_NW_D64 8
 #endif
 
-// Row-major tile of `rows` rows of D bf16 features; 16-byte chunks XOR-swizzled
-// by row (conflict-free fragment reads, as in the forward kernel).
+// Row-major tile, D bf16 features per row.  16-byte chunk c of row r sits at
+// physical chunk c ^ rm_swz<D>(r), chosen so that both fragment reads are free
+// of bank conflicts:
+//   * 16-byte reads of one chunk in 16 consecutive rows (each 16-lane phase),
+//     the score products' operands: the swizzle is a bijection over 16 rows
+//     (over the 8 rows of each parity for D = 64, two rows per bank line);
+//   * 8-byte transposed reads (ds_read_b64_tr_b16), the accumulation products'
+//     operands: 16-lane group a reads chunks 2m and 2m+1 of rows 4a .. 4a+3
+//     (mod 16), and two groups share a cycle, as (0,1) and (2,3) or as (0,2)
+//     and (1,3).  A row's two chunks land on the slot pair p = rm_swz >> 1, so
+//     the pairs of rows in groups sharing a cycle must differ: groups 0 and 3
+//     take one half of the pair indices, groups 1 and 2 the other (a Gray-code
+//     split), and the low bit separates 0 from 3 and 1 from 2.
+// D = 128: row r = 4a + i, p = 4 [a in {1,2}] + i, swizzle 2p + [a >= 2].
+// D = 64: row r = 4a + 2i + parity, p = 2 [a in {1,2}] + i, swizzle 2p + [a >= 2].
+template <int D>
+__device__ __forceinline__ int rm_swz(int r) {
+  const int a = (r >> 2) & 3;
+  const int mid = (a ^ (a >> 1)) & 1;            // a is 1 or 2
+  if constexpr (D == 128) return 2 * (4 * mid + (r & 3)) + (a >> 1);
+  else return 2 * (2 * mid + ((r >> 1) & 1)) + (a >> 1);
+}
 template <int D>
 __device__ __forceinline__ int rm_off(int r, int c) {
+  return r * D + ((c ^ rm_swz<D>(r)) << 3);
+}
+
+// The query-stationary kernel's K and V tiles: 16-byte chunks XOR-swizzled by
+// row (its fragment reads are all 16-byte reads of 16 consecutive rows), and
+// its K^T operand comes from a staged transposed tile (one row of W = 64
+// positions per feature) with the forward's V^T swizzle c ^ (f & 7), so that
+// eight lanes at a time hit eight different 16-byte slots of a bank line.  (A
+// transposed LDS read of K would save the staging but needs eight more live
+// address registers, which push this kernel past 256 VGPRs at d = 128.)
+template <int D>
+__device__ __forceinline__ int rm_off_q(int r, int c) {
   return r * D + ((c ^ (r & (D / 8 - 1))) << 3);
 }
-// Transposed tile, one row of W positions per feature (W = 64 or 32).  A
-// fragment read takes one 16-byte chunk from each of 16 consecutive rows; eight
-// lanes at a time must hit eight different 16-byte slots of a 128-byte bank
-// line.  For W = 64 (128-byte rows) the chunk swizzle is the forward's V^T
-// swizzle c ^ (f & 7).  For W = 32 a row is half a line: rows f and f+1 fill the
-// two halves, so among the even (or odd) rows of an 8-row group the chunk must
-// differ, c ^ ((f >> 1) & 3).
-template <int W>
-__device__ __forceinline__ int tr_swz(int f) {
-  if constexpr (W == 64) return f & 7;
-  else return (f >> 1) & 3;
-}
-template <int W>
-__device__ __forceinline__ int tr_off(int f, int c) {
-  return f * W + ((c ^ tr_swz<W>(f)) << 3);
+__device__ __forceinline__ int tr_off64(int f, int c) { return f * 64 + ((c ^ (f & 7)) << 3); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposed fragment of a row-major tile: for lane (c16, g4), feature f0 + c16
+// of rows r0 + 4 g4 + 0..3 and r0 + 16 + 4 g4 + 0..3, the order in which a lane
+// holds rows of two stacked 16-row score blocks.  ds_read_b64_tr_b16 (measured
+// on gfx950): in each 16-lane group, lane i receives element i mod 4 of the
+// 8-byte chunks addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12; so lane j
+// addresses features f0 + 4 (j mod 4) .. +3 of row (j / 4) of the 4-row block.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int r0, int f0, int c16, int g4) {
+  const int c = (f0 >> 3) + ((c16 & 3) >> 1);    // logical chunk of features f0 + 4 (c16 & 3)
+  const int e = 4 * (c16 & 1);                   // their first element within the chunk
+  const int r = r0 + 4 * g4 + (c16 >> 2);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + rm_off<D>(r, c) + e));
+  const s16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + rm_off<D>(r + 16, c) + e));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // ------------------------------------------------------------------- prep
@@ -232,17 +269,15 @@ template <int D, int NW, int KB>
 __global__ __launch_bounds__(64 * NW, 1)
 void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, const __bf16* __restrict__ rho,
-                     const __bf16* __restrict__ do16, const __bf16* __restrict__ qT,
-                     const __bf16* __restrict__ rT, const __bf16* __restrict__ dT,
-                     const f32x4* __restrict__ stats, const float* __restrict__ gate,
-                     float* __restrict__ dk, float* __restrict__ dv, int H, int L, int BH,
+                     const __bf16* __restrict__ do16, const f32x4* __restrict__ stats,
+                     const float* __restrict__ gate, float* __restrict__ dk,
+                     float* __restrict__ dv, int H, int L, int BH,
                      int n_kblk, float sl2, float scale) {
   constexpr int KSTEPS = D / 32;
   constexpr int FB = D / 16;
   constexpr int BK = 16 * KB * NW;                 // keys per workgroup
   constexpr int RM = BW_BQ * D;                    // elements of a row-major step tile
-  constexpr int TR = D * BW_BQ;                    // elements of a transposed step tile
-  constexpr int STAGE = 3 * RM + 3 * TR + 64 * 8;  // + 64 stats records (1 KB)
+  constexpr int STAGE = 3 * RM + 64 * 8;           // + 64 stats records (1 KB)
   constexpr int RMBLK = RM * 2 / 1024;             // 1-KB blocks per tile
   static_assert(RMBLK % NW == 0, "tile blocks per wave");
   __shared__ __align__(16) uint16_t smem[2 * STAGE];
@@ -259,7 +294,6 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int k0 = kblk * BK;
   const int kw0 = k0 + 16 * KB * wave;
   const size_t head = (size_t)bh * L * D;
-  const int n64 = (L + BW_T - 1) / BW_T;
   const float ng = -gate[h];
   const float inv_scale = 1.0f / scale;
 
@@ -292,21 +326,13 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
   // per-lane byte offsets of this wave's 1-KB blocks (swizzle included)
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t rmoff[RMBLK / NW], troff[RMBLK / NW];
+  uint32_t rmoff[RMBLK / NW];
 #pragma unroll
   for (int i = 0; i < RMBLK / NW; ++i) {
+    // physical chunk pc of LDS row r holds logical chunk pc ^ rm_swz(r)
     const int e = (i * NW + wave) * 512 + 8 * lane;
-    {
-      const int r = e / D, pc = (e % D) / 8;
-      rmoff[i] = (uint32_t)((r * D + ((pc ^ (r & (D / 8 - 1))) << 3)) * 2);
-    }
-    {
-      const int f = e / BW_BQ, pc = (e % BW_BQ) / 8;
-      // physical chunk pc of LDS row f holds logical chunk pc ^ tr_swz(f); the
-      // global tile row of feature f holds 64 positions, this step's 32 start
-      // at the half selected by the base pointer
-      troff[i] = (uint32_t)((f * BW_T + ((pc ^ tr_swz<BW_BQ>(f)) << 3)) * 2);
-    }
+    const int r = e / D, pc = (e % D) / 8;
+    rmoff[i] = (uint32_t)((r * D + ((pc ^ rm_swz<D>(r)) << 3)) * 2);
   }
   const int n_qs = (L + BW_BQ - 1) / BW_BQ;
   const int qs0 = k0 / BW_BQ;
@@ -322,20 +348,9 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       for (int i = 0; i < RMBLK / NW; ++i)
         buffer_load_lds16(srcs[m], rows * D * 2, st + m * RM + (i * NW + wave_u) * 512, rmoff[i]);
     }
-    // transposed tiles: staged [bh][n64][D][64], this step is half (qs & 1)
-    const size_t toff = ((size_t)bh * n64 + (qs >> 1)) * (size_t)(D * BW_T) + (qs & 1) * BW_BQ;
-    const __bf16* trs[3] = {qT + toff, rT + toff, dT + toff};
-    const int tbytes = (D * BW_T - (qs & 1) * BW_BQ) * 2;
-#pragma unroll
-    for (int m = 0; m < 3; ++m) {
-#pragma unroll
-      for (int i = 0; i < RMBLK / NW; ++i)
-        buffer_load_lds16(trs[m], tbytes, st + 3 * RM + m * TR + (i * NW + wave_u) * 512,
-                          troff[i]);
-    }
     // statistics of rows q0 .. q0+63 (the second half is not used)
     if (wave_u == 0)
-      buffer_load_lds16(stats + (size_t)bh * L + q0, (L - q0) * 16, st + 3 * RM + 3 * TR,
+      buffer_load_lds16(stats + (size_t)bh * L + q0, (L - q0) * 16, st + 3 * RM,
                         (uint32_t)(16 * lane));
   };
 
@@ -346,10 +361,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const uint16_t* Qs = st;
     const uint16_t* Rs = st + RM;
     const uint16_t* Os = st + 2 * RM;
-    const uint16_t* QTs = st + 3 * RM;
-    const uint16_t* RTs = st + 3 * RM + TR;
-    const uint16_t* OTs = st + 3 * RM + 2 * TR;
-    const f32x4* Ss = reinterpret_cast<const f32x4*>(st + 3 * RM + 3 * TR);
+    const f32x4* Ss = reinterpret_cast<const f32x4*>(st + 3 * RM);
     const int q0 = qs * BW_BQ;
     // S = Q K^T, R = rho K^T, Delta = dO V^T for 32 queries x 16*KB keys; lane
     // holds key kw0 + 16 kb + c16 and queries q0 + 16 qb + 4 g4 + j
@@ -377,8 +389,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       }
     }
     // W~, dS/scale, dR/scale in bf16 (dK = scale (Q^T dS/scale + rho^T dR/scale)):
-    // element e = 4 qb + j of a key's 8 queries, the position order of the staged
-    // transposed tiles
+    // element e = 4 qb + j of a key's 8 queries, the row order of tr_frag
     bf16x8 wtp[KB], dsp[KB], drp[KB];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -402,10 +413,9 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     // dV^T += dO^T W~,  dK^T += Q^T dS' + rho^T dR
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb) {
-      const int off = tr_off<BW_BQ>(16 * fb + c16, g4);
-      const bf16x8 ao = *reinterpret_cast<const bf16x8*>(OTs + off);
-      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(QTs + off);
-      const bf16x8 ar = *reinterpret_cast<const bf16x8*>(RTs + off);
+      const bf16x8 ao = tr_frag<D>(Os, 0, 16 * fb, c16, g4);
+      const bf16x8 aq = tr_frag<D>(Qs, 0, 16 * fb, c16, g4);
+      const bf16x8 ar = tr_frag<D>(Rs, 0, 16 * fb, c16, g4);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         dv_acc[kb][fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, wtp[kb], dv_acc[kb][fb], 0, 0, 0);
@@ -517,7 +527,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     {
       const int f = e / BW_T, pc = (e % BW_T) / 8;
-      troff[i] = (uint32_t)((f * BW_T + ((pc ^ tr_swz<BW_T>(f)) << 3)) * 2);
+      troff[i] = (uint32_t)((f * BW_T + ((pc ^ (f & 7)) << 3)) * 2);
     }
   }
   const int last_q = min(q0 + BR, L) - 1;
@@ -552,7 +562,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
-        const int off = rm_off<D>(16 * kb + c16, 4 * kk + g4);
+        const int off = rm_off_q<D>(16 * kb + c16, 4 * kk + g4);
         const bf16x8 ak = *reinterpret_cast<const bf16x8*>(Ks + off);
         const bf16x8 av = *reinterpret_cast<const bf16x8*>(Vs + off);
         if (kk == 0) {
@@ -585,7 +595,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       // dQ^T += K^T (dS/scale)^T,  drho^T += K^T dR^T over the 32 keys of group t
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(KTs + tr_off<BW_T>(16 * fb + c16, 4 * t + g4));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(KTs + tr_off64(16 * fb + c16, 4 * t + g4));
         dq_acc[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dsp, dq_acc[fb], 0, 0, 0);
         dr_acc[fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, drp, dr_acc[fb], 0, 0, 0);
       }
@@ -619,8 +629,10 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 hipError_t launch_stage_t_bf16(const void* x, void* xt, int BH, int L, int d, hipStream_t s);
 
 // Scratch layout of one backward call, in bytes from the workspace start.
+hipError_t launch_stage_t_bf16(const void* x, void* xt, int BH, int L, int d, hipStream_t s);
+
 struct BwdScratch {
-  size_t do16, dT, qT, rT, kT, stats, gpart, total;
+  size_t do16, kT, stats, gpart, total;
 };
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 BwdScratch bwd_scratch(int B, int H, int L, int d) {
@@ -630,10 +642,7 @@ BwdScratch bwd_scratch(int B, int H, int L, int d) {
   const size_t tr = align256(BH * n64 * BW_T * d * 2);
   BwdScratch w;
   w.do16 = 0;
-  w.dT = w.do16 + rm;
-  w.qT = w.dT + tr;
-  w.rT = w.qT + tr;
-  w.kT = w.rT + tr;
+  w.kT = w.do16 + rm;
   w.stats = w.kT + tr;
   w.gpart = w.stats + align256(BH * L * 16);
   w.total = w.gpart + align256(BH * n64 * 4);
@@ -642,16 +651,15 @@ BwdScratch bwd_scratch(int B, int H, int L, int d) {
 
 template <int D, int NW, int KB>
 static void launch_dkdv_t(const void* q, const void* k, const void* v, const void* rho,
-                          const void* do16, const void* qT, const void* rT, const void* dT,
-                          const void* stats, const float* gate, float* dk, float* dv, int BH,
+                          const void* do16, const void* stats, const float* gate, float* dk,
+                          float* dv, int BH,
                           int H, int L, float sl2, float scale, hipStream_t s) {
   constexpr int BK = 16 * KB * NW;
   const int n_kblk = (L + BK - 1) / BK;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, KB>), dim3((unsigned)(BH * n_kblk)), dim3(64 * NW),
                      0, s, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                     (const __bf16*)rho, (const __bf16*)do16, (const __bf16*)qT,
-                     (const __bf16*)rT, (const __bf16*)dT, (const f32x4*)stats, gate, dk, dv, H,
-                     L, BH, n_kblk, sl2, scale);
+                     (const __bf16*)rho, (const __bf16*)do16, (const f32x4*)stats, gate, dk, dv,
+                     H, L, BH, n_kblk, sl2, scale);
 }
 
 template <int D, int NW>
@@ -677,9 +685,6 @@ hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, 
   const BwdScratch w = bwd_scratch(B, H, L, d);
   char* base = static_cast<char*>(ws);
   void* do16 = base + w.do16;
-  void* dT = base + w.dT;
-  void* qT = base + w.qT;
-  void* rT = base + w.rT;
   void* kT = base + w.kT;
   f32x4* stats = reinterpret_cast<f32x4*>(base + w.stats);
   float* gpart = reinterpret_cast<float*>(base + w.gpart);
@@ -693,21 +698,18 @@ hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, 
                        out, corr, lse, rbar, gate, (__bf16*)do16, stats, gpart, H, L, n64);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const void* srcs[4] = {do16, q, rho, k};
-  void* dsts[4] = {dT, qT, rT, kT};
-  for (int i = 0; i < 4; ++i) {
-    e = launch_stage_t_bf16(srcs[i], dsts[i], BH, L, d, s);
-    if (e != hipSuccess) return e;
-  }
+  // K^T tiles for the query-stationary kernel (the key-stationary one reads its
+  // transposed operands straight from its row-major tiles)
+  e = launch_stage_t_bf16(k, kT, BH, L, d, s);
+  if (e != hipSuccess) return e;
   if (d == 128) {
-    launch_dkdv_t<128, PLX_BW_KV_NW_D128, PLX_BW_KV_KB_D128>(q, k, v, rho, do16, qT, rT, dT,
-                                                              stats, gate, dk, dv, BH, H, L,
-                                                              sl2, scale, s);
+    launch_dkdv_t<128, PLX_BW_KV_NW_D128, PLX_BW_KV_KB_D128>(q, k, v, rho, do16, stats, gate, dk,
+                                                              dv, BH, H, L, sl2, scale, s);
     launch_dq_t<128, PLX_BW_Q_NW_D128>(q, k, v, rho, do16, kT, stats, gate, dq, drho, BH, H, L,
                                        sl2, scale, s);
   } else {
-    launch_dkdv_t<64, PLX_BW_KV_NW_D64, PLX_BW_KV_KB_D64>(q, k, v, rho, do16, qT, rT, dT, stats,
-                                                          gate, dk, dv, BH, H, L, sl2, scale, s);
+    launch_dkdv_t<64, PLX_BW_KV_NW_D64, PLX_BW_KV_KB_D64>(q, k, v, rho, do16, stats, gate, dk,
+                                                          dv, BH, H, L, sl2, scale, s);
     launch_dq_t<64, PLX_BW_Q_NW_D64>(q, k, v, rho, do16, kT, stats, gate, dq, drho, BH, H, L,
                                      sl2, scale, s);
   }
