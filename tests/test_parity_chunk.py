@@ -118,6 +118,14 @@ def test_chunk_workload_sampled(name):
     err = float(np.max(np.abs(got[rows] - ref[rows])))
     print(f"{name}: {len(rows)} sampled rows, max-abs {err:.3e}", flush=True)
     assert err <= TOL
+    # the serving path the benchmark also times: V from a staged cache (for
+    # one-tile chunks with non-temporal tile loads), the same bits
+    plx = _plx()
+    vt = plx.prefill_stage_v(inp["vcache"])
+    staged = plx.prefill_chunk(inp["q"], inp["kcache"], None, inp["rho"], inp["gate"],
+                               inp["cu_q"], inp["ctx"], inp["max_q"], vt_cache=vt)
+    torch.cuda.synchronize()
+    assert torch.equal(staged, out)
 
 
 @pytest.mark.parametrize("d", [64, 128])
