@@ -195,3 +195,27 @@ def test_backward_partial_head_group(d):
           flush=True)
     for n, e in errs.items():
         assert e <= 2e-2, n
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_backward_random_shapes(seed):
+    """Seeded random shapes: B 1-2, H 1-36 (partial head groups), L 1-260, d 64
+    or 128; every gradient against the oracle."""
+    rng = np.random.default_rng(2300 + seed)
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 37))
+    L = int(rng.integers(1, 261))
+    d = int(rng.choice([64, 128]))
+    if B * H * L > 4000:
+        L = max(1, 4000 // (B * H))
+    inp = wl.prefill_inputs(B, H, L, d, "bf16", seed=2400 + seed, device="cuda", rho_std=0.5,
+                            gate=("uniform", 0.2, 1.0))
+    dout = _dout((B, H, L, d), 2500 + seed)
+    _, grads = _run(inp, dout)
+    h = {n: inp[n].cpu() for n in inp}
+    ref = po.prefill_backward(h["q"], h["k"], h["v"], h["rho"], h["gate"], dout.cpu())
+    errs = {n: _rel_err(_np(t), ref[n]) for n, t in zip(GRADS, grads[:4])}
+    errs["dgate"] = _rel_err(_np(grads[4]), ref["dgate"])
+    print(f"random {seed}: B{B} H{H} L{L} d{d}: " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()),
+          flush=True)
+    for n, e in errs.items():
+        assert e <= 2e-2, n

@@ -148,3 +148,27 @@ def test_widest_grid():
     err = max(_maxerr(out[b, 0], ref[b, 0]) for b in streams)
     print(f"decode B*H=65535: max-abs over sampled streams {err:.3e}", flush=True)
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_decode_random_shapes(seed):
+    """Seeded random shapes: B 1-6, H 1-8, Lmax 1-5000 with ragged lengths
+    (including 0 and Lmax), d 64 or 128, bf16 or fp32, the library's split or a
+    random multiple of 64; every stream against the oracle."""
+    rng = np.random.default_rng(2600 + seed)
+    B, H = int(rng.integers(1, 7)), int(rng.integers(1, 9))
+    Lmax = int(rng.integers(1, 5001))
+    d = int(rng.choice([64, 128]))
+    dtype = "f32" if seed % 4 == 1 else "bf16"
+    lens = [int(x) for x in rng.integers(0, Lmax + 1, B)]
+    lens[0] = Lmax
+    if B > 1:
+        lens[-1] = 0
+    split = 0 if seed % 2 == 0 else 64 * int(rng.integers(1, 33))
+    inp = wl.decode_inputs(B, H, Lmax, d, dtype, seed=2700 + seed, device="cuda",
+                           rho_std=0.5, seqlens=lens)
+    out = _run(inp, split_keys=split)
+    err = _maxerr(_host(out).double().numpy(), _oracle(inp))
+    print(f"random {seed}: {dtype} B{B} H{H} Lmax{Lmax} d{d} lens{lens} split {split}: "
+          f"max-abs {err:.3e}", flush=True)
+    assert err <= TOL[dtype]

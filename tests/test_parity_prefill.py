@@ -234,3 +234,22 @@ def test_partial_head_group_d64(B, H):
     err = float(np.max(np.abs(out.cpu().double().numpy() - ref)))
     print(f"partial head group B{B} H{H}: max-abs {err:.3e}", flush=True)
     assert err <= 2e-2
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_prefill_random_shapes(seed):
+    """Seeded random shapes: B 1-3, H 1-20 (partial head groups at d=64), L
+    1-700, d 64 or 128, bf16 or fp32; every element against the oracle."""
+    rng = np.random.default_rng(2100 + seed)
+    B, H = int(rng.integers(1, 4)), int(rng.integers(1, 21))
+    L = int(rng.integers(1, 701))
+    d = int(rng.choice([64, 128]))
+    dtype = "f32" if seed % 4 == 3 else "bf16"
+    if B * H * L > 6000:                      # keep the fp64 oracle to seconds
+        L = max(1, 6000 // (B * H))
+    inp = wl.prefill_inputs(B, H, L, d, dtype, seed=2200 + seed, device="cuda", rho_std=0.5,
+                            gate=("uniform", 0.2, 1.0))
+    out = _run(inp)
+    err = _maxerr(out, _oracle_all(inp))
+    print(f"random {seed}: {dtype} B{B} H{H} L{L} d{d}: max-abs {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
