@@ -176,9 +176,11 @@ int parallax_decode_default_split(int B, int H, int Lmax, int d);
  * where split_keys >= Lmax means no split.  Other values are PLX_EINVAL.
  * The workspace (at least parallax_prefill_chunk_workspace_bytes(B, H, T,
  * Lmax, max_q, d, split_keys) bytes, or NULL to let the library allocate on
- * `stream`) holds the fp16 V^T tiles of the cache rows the chunks read and,
- * when split, the partial states (T*H*S records of 2d+4 floats,
- * S = ceil(ceil(Lmax/64) / (split_keys/64))). */
+ * `stream` when it needs any) holds the fp16 V^T tiles of the cache rows the
+ * chunks read and, when split, the partial states (T*H*S records of 2d+4
+ * floats, S = ceil(ceil(Lmax/64) / (split_keys/64))).  At d = 128 with
+ * max_q <= 16 the kernel converts the bf16 V tiles itself, so there are no
+ * V^T tiles and, without a split, the size is 0. */
 size_t parallax_prefill_chunk_workspace_bytes(int B, int H, int T, int Lmax, int max_q, int d,
                                               int split_keys);
 

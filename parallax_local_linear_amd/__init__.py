@@ -268,10 +268,11 @@ def prefill_chunk(q, kcache, vcache, rho, gate, cu_q, ctx, max_q, scale=None, ou
         return out
     _check("vcache", vcache, torch.bfloat16, (B, H, Lmax, d), q.device)
     wsb = int(lib().parallax_prefill_chunk_workspace_bytes(B, H, T, Lmax, mq, d, sk))
-    if workspace is None:
+    if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
-    _check("workspace", workspace, device=q.device)
-    wsb = workspace.numel() * workspace.element_size()
+    if workspace is not None:
+        _check("workspace", workspace, device=q.device)
+        wsb = workspace.numel() * workspace.element_size()
     _launch(q.device, "parallax_prefill_chunk", _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(rho),
             _ptr(gate), _ptr(out), _ptr(cu_q), _ptr(ctx), B, H, T, Lmax, mq, d,
             _scale(scale, d), PLX_BF16, sk, _ptr(workspace), wsb)

@@ -43,6 +43,7 @@ hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, c
 int chunk_default_split(int B, int H, int Lmax, int max_q, int d);
 int chunk_num_splits(int Lmax, int split_keys);
 size_t chunk_part_bytes(int T, int H, int Lmax, int d, int split_keys);
+bool chunk_fuses_v(int d, int max_q);
 long long chunk_split_blocks(int B, int H, int Lmax, int max_q, int d, int split_keys);
 hipError_t launch_stage_v_rows(const void* vc, void* vt, const int* cu_q, const int* ctx, int B,
                                int H, int T, int Lmax, int max_q, int d, bool new_rows_only,
@@ -152,6 +153,12 @@ float eff_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / std::s
 size_t vt_bytes(int B, int H, int L, int d) {
   const size_t n_kt = (size_t)((L + kTileKeys - 1) / kTileKeys);
   return (size_t)B * H * n_kt * kTileKeys * d * 2;
+}
+
+// Bytes ahead of the split records in a per-call chunk workspace: the staged
+// V^T tiles, unless the kernel converts the raw V tiles itself.
+size_t chunk_vt_off(int B, int H, int Lmax, int max_q, int d) {
+  return plx::chunk_fuses_v(d, max_q) ? 0 : align256(vt_bytes(B, H, Lmax, d));
 }
 
 size_t part_bytes(int B, int H, int Lmax, int d, int C) {
@@ -444,7 +451,7 @@ size_t parallax_prefill_chunk_workspace_bytes(int B, int H, int T, int Lmax, int
   if (B <= 0 || H <= 0 || T <= 0 || Lmax <= 0 || max_q <= 0 || (d != 64 && d != 128)) return 0;
   if (split_keys < 0 || split_keys % 64 != 0) return 0;
   const int keys = split_keys ? split_keys : plx::chunk_default_split(B, H, Lmax, max_q, d);
-  return align256(vt_bytes(B, H, Lmax, d)) + plx::chunk_part_bytes(T, H, Lmax, d, keys);
+  return chunk_vt_off(B, H, Lmax, max_q, d) + plx::chunk_part_bytes(T, H, Lmax, d, keys);
 }
 
 size_t parallax_prefill_chunk_vt_workspace_bytes(int B, int H, int T, int Lmax, int max_q, int d,
@@ -477,12 +484,11 @@ int parallax_prefill_chunk(const void* q, const void* kcache, const void* vcache
   hipStream_t s = (hipStream_t)stream;
   Scratch scratch;
   void* ws = nullptr;
-  const size_t vt_off = align256(vt_bytes(B, H, Lmax, d));
-  if (!get_workspace(workspace, workspace_bytes,
-                     vt_off + plx::chunk_part_bytes(T, H, Lmax, d, keys), s, &scratch, &ws, fn,
-                     &st))
+  const size_t vt_off = chunk_vt_off(B, H, Lmax, max_q, d);
+  const size_t need = vt_off + plx::chunk_part_bytes(T, H, Lmax, d, keys);
+  if (need > 0 && !get_workspace(workspace, workspace_bytes, need, s, &scratch, &ws, fn, &st))
     return st;
-  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + vt_off);
+  float* part = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + vt_off) : nullptr;
   hipError_t e = plx::launch_prefill_chunk(q, kcache, vcache, rho, gate, out, cu_q, ctx, B, H, T,
                                            Lmax, max_q, d, eff_scale(scale, d), keys, ws, part,
                                            s);

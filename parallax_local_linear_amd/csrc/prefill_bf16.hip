@@ -48,6 +48,8 @@
 namespace plx {
 
 constexpr int PF_BC = 64;       // keys per tile
+// s_waitcnt immediate for "lgkmcnt(0)" with vmcnt and expcnt left unconstrained
+constexpr int kWaitLgkm0 = 0xC07F;
 // waves per workgroup (16 queries each), per head dimension
 #ifndef PLX_PF_NW_D128
 #define PLX_PF_NW_D128 4
@@ -90,6 +92,11 @@ constexpr int PF_BC = 64;       // keys per tile
 // +13 %.
 #ifndef PLX_CHUNK_NT
 #define PLX_CHUNK_NT 1
+#endif
+// Per-call chunked prefill at d = 128 with at most 16 queries per chunk: convert
+// the raw V tiles in the kernel (1) instead of a staging pass (0).
+#ifndef PLX_CHUNK_FUSEV
+#define PLX_CHUNK_FUSEV 1
 #endif
 // The same three choices for the softmax-only variant (correction compiled out),
 // tuned on their own: without R, T and their accumulators the d=128 kernel
@@ -186,8 +193,13 @@ __device__ __forceinline__ void chunk_geometry(const ChunkArgs& ca, int b, int* 
 // offset by the chunk's cache position.  SPLIT (with VARLEN) walks only the key
 // tiles of one split and writes the unnormalised state of every row (m, l, c,
 // sum p v, sum p r v) to ca.part for chunk_combine_kernel.  NT loads the K and
-// V tiles with the non-temporal cache policy.
-template <int D, int NW, bool PIPE, bool CORR, bool SAVE, bool VARLEN, bool SPLIT, bool NT>
+// V tiles with the non-temporal cache policy.  FUSEV (chunks of at most 16
+// queries, so wave 0 is the only one with queries; plain schedule) reads V
+// straight from the bf16 cache: each raw tile is staged in LDS like K, and the
+// other waves convert it to the fp16 V^T tile layout (the layout stage_v
+// writes, the same values) while wave 0 computes the tile's scores.
+template <int D, int NW, bool PIPE, bool CORR, bool SAVE, bool VARLEN, bool SPLIT, bool NT,
+          bool FUSEV>
 __global__ __launch_bounds__(64 * NW, CORR ? (D == 64 ? PLX_PF_MINW_D64 : PLX_PF_MINW_D128)
                                           : (D == 64 ? PLX_SM_MINW_D64 : PLX_SM_MINW_D128))
 void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -199,13 +211,16 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   static_assert(CORR || !SAVE, "the training statistics belong to the Parallax kernel");
   static_assert(!(SAVE && VARLEN), "the training statistics are for whole sequences");
   static_assert(!SPLIT || (VARLEN && CORR), "key splits are for the chunked prefill");
+  static_assert(!FUSEV || (VARLEN && !PIPE && NW > 1), "fused V conversion: chunks, plain");
   using LY = PfLayout<D>;
   constexpr int PF_BR = 16 * NW;                         // queries per workgroup
   constexpr int PF_THREADS = 64 * NW;
   constexpr int KSTEPS = D / 32;                         // MFMA steps over features
   constexpr int FB = D / 16;                             // 16-feature output blocks
 
-  __shared__ __align__(16) uint16_t smem[2 * LY::STAGE];
+  // FUSEV: K and raw V double-buffered, one V^T tile
+  constexpr int SMEM = FUSEV ? 4 * LY::K_ELEMS + LY::V_ELEMS : 2 * LY::STAGE;
+  __shared__ __align__(16) uint16_t smem[SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -256,7 +271,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     qbase = ((size_t)c0 * H + h) * D;
     qstride = (size_t)H * D;
     kh = k + (size_t)bh * ca.Lmax * D;
-    vth = vt + (size_t)bh * ca.n64max * (D * PF_BC);
+    // staged V^T tiles; FUSEV: the raw bf16 cache rows of this head, like K
+    vth = FUSEV ? vt + (size_t)bh * ca.Lmax * D : vt + (size_t)bh * ca.n64max * (D * PF_BC);
   }
   const int n_k = pos0 + n_q;
 
@@ -352,6 +368,16 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   };
   const char* vbase = reinterpret_cast<const char*>(vth);
   auto load_v = [&](int kt, int buf) {
+    if constexpr (FUSEV) {
+      // raw bf16 rows of the cache, laid out like K
+      const int rows = min(PF_BC, n_k - kt * PF_BC);
+      const char* tile = vbase + (size_t)kt * PF_BC * D * 2;
+#pragma unroll
+      for (int i = 0; i < KBLK / NW; ++i)
+        tile_load16(tile, rows * D * 2,
+                    smem + 2 * LY::K_ELEMS + buf * LY::K_ELEMS + (i * NW + wave_u) * 512, koff[i]);
+      return;
+    }
     const char* tile = vbase + (size_t)kt * (D * PF_BC) * 2;
 #pragma unroll
     for (int i = 0; i < VBLK / NW; ++i)
@@ -447,7 +473,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // value products O^T += V^T P^T, A_r^T += V^T T^T of tile kt_.
   auto softmax_pv = [&](auto vbuf, f32x4 (&sa)[4], f32x4 (&ra)[4]) {
     const float m_use = m_run;
-    const uint16_t* vs = smem + 2 * LY::K_ELEMS + (int)vbuf * LY::V_ELEMS;
+    const uint16_t* vs = FUSEV ? smem + 4 * LY::K_ELEMS
+                               : smem + 2 * LY::K_ELEMS + (int)vbuf * LY::V_ELEMS;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f16x8 pf, rf, tf;
@@ -472,6 +499,24 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         if constexpr (CORR)
           acc_r[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, tf, acc_r[fb], 0, 0, 0);
       }
+    }
+  };
+  // FUSEV: raw V tile `buf` (bf16, K's layout) -> the fp16 V^T tile, by waves
+  // 1 .. NW-1.  Chunk c of V^T row f holds keys vt_key_of_pos(8c .. 8c+7) of
+  // feature f, converted bf16 -> fp32 -> fp16 (RNE) as stage_v does.
+  auto convert_v = [&](int buf) {
+    const uint16_t* raw = smem + 2 * LY::K_ELEMS + buf * LY::K_ELEMS;
+    uint16_t* vtl = smem + 4 * LY::K_ELEMS;
+    for (int idx = tid - 64; idx < D * PF_BC / 8; idx += 64 * (NW - 1)) {
+      const int f = idx >> 3, c = idx & 7;
+      f16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = vt_key_of_pos(8 * c + e);
+        const uint32_t bits = raw[LY::k_off(key, f >> 3) + (f & 7)];
+        o[e] = (_Float16)__uint_as_float(bits << 16);
+      }
+      *reinterpret_cast<f16x8*>(vtl + LY::v_off(f, c)) = o;
     }
   };
   // Pipelined step: the score MFMAs of tile kt_+1, the softmax and value MFMAs
@@ -528,7 +573,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         } else {
           softmax_pv(par, cs, cr);
         }
-      } else {
+      } else if constexpr (!FUSEV) {
         scores(par, cs, cr);
         const float m_tile = needs_mask(kt) ? tile_max(cs, kt, std::true_type{})
                                             : tile_max(cs, kt, std::false_type{});
@@ -536,6 +581,27 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         rescale_to(m_tile);
         softmax_pv(par, cs, cr);
       }
+    }
+    if constexpr (FUSEV) {
+      // wave 0: the scores of tile kt; the other waves: its V^T tile
+      if (wave_u == 0) {
+        if (kt < w_end) {
+          scores(par, cs, cr);
+          const float m_tile = needs_mask(kt) ? tile_max(cs, kt, std::true_type{})
+                                              : tile_max(cs, kt, std::false_type{});
+          if (kt == t_beg) m_run = m_tile;      // accumulators are still zero
+          rescale_to(m_tile);
+        }
+      } else {
+        convert_v(P);
+      }
+      // V^T complete: this wave's LDS writes are done (lgkmcnt); a bare barrier,
+      // since __syncthreads() would also wait for the loads of tile kt+1
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (kt < w_end) softmax_pv(par, cs, cr);
     }
     wait_loads();
     __syncthreads();
@@ -692,7 +758,7 @@ struct TrainOut {
 };
 
 template <int D, int NW, bool PIPE, bool CORR, bool SAVE = false, bool VARLEN = false,
-          bool SPLIT = false, bool NT = false>
+          bool SPLIT = false, bool NT = false, bool FUSEV = false>
 static hipError_t launch_prefill_t(const void* q, const void* k, const void* vt,
                                    const void* rho, const float* gate, float* out, int B,
                                    int H, int L, float sl2, hipStream_t s, TrainOut tr = {},
@@ -700,7 +766,7 @@ static hipError_t launch_prefill_t(const void* q, const void* k, const void* vt,
   const int BH = B * H;
   const int n_qt = ((VARLEN ? ca.max_q : L) + 16 * NW - 1) / (16 * NW);
   const unsigned n_blocks = (unsigned)BH * (unsigned)n_qt * (SPLIT ? (unsigned)ca.n_split : 1u);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, PIPE, CORR, SAVE, VARLEN, SPLIT, NT>),
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, PIPE, CORR, SAVE, VARLEN, SPLIT, NT, FUSEV>),
                      dim3(n_blocks), dim3(64 * NW), 0, s, (const __bf16*)q,
                      (const __bf16*)k, (const _Float16*)vt, (const __bf16*)rho, gate, out, tr.lse,
                      tr.rbar, tr.corr, H, L, BH, n_qt, sl2, ca);
@@ -838,6 +904,11 @@ size_t chunk_part_bytes(int T, int H, int Lmax, int d, int split_keys) {
   return ns > 1 ? (size_t)T * H * ns * (2 * d + 4) * sizeof(float) : 0;
 }
 
+// Whether a per-call chunked prefill reads V straight from the bf16 cache and
+// converts its tiles in the kernel (no staging pass, no staged V^T workspace):
+// d = 128 with chunks of at most 16 queries, one busy wave per workgroup.
+bool chunk_fuses_v(int d, int max_q) { return PLX_CHUNK_FUSEV && d == 128 && max_q <= 16; }
+
 // The chunked-prefill kernel at head dimension D (split-KV or not, NT cache policy).
 template <int D, bool SPLIT, bool NT>
 static hipError_t launch_chunk_t(const void* q, const void* kc, const void* vt, const void* rho,
@@ -860,15 +931,18 @@ hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, c
   const float sl2 = scale * kLog2e;
   const int n64 = (Lmax + PF_BC - 1) / PF_BC;
   ChunkArgs ca{cu_q, ctx, T, Lmax, max_q, n64, 0};
-  if (vc) {
+  // Per-call V at d = 128 with one-wave chunks: the kernel converts the raw V
+  // tiles itself (no staging pass, and vt is not used).
+  const bool fuse = vc != nullptr && chunk_fuses_v(d, max_q);
+  if (vc && !fuse) {
     hipError_t e = launch_stage_v_rows(vc, vt, cu_q, ctx, B, H, T, Lmax, max_q, d, false, s);
     if (e != hipSuccess) return e;
   }
   // Non-temporal tile loads when each sequence's chunk fits one query tile (no
-  // workgroup re-reads a K/V tile) and V comes from the caller's staged cache.
-  // With per-call staging the V^T tiles were written just before and the
-  // default policy measured as fast or faster.
-  const bool nt = PLX_CHUNK_NT && vc == nullptr &&
+  // workgroup re-reads a K/V tile) and V comes from the caller's staged cache
+  // or, fused, straight from the V cache.  With per-call staging the V^T tiles
+  // were written just before and the default policy measured as fast or faster.
+  const bool nt = PLX_CHUNK_NT && (vc == nullptr || fuse) &&
                   max_q <= 16 * (d == 128 ? PLX_PF_NW_D128 : PLX_PF_NW_D64);
   const int n_split = chunk_num_splits(Lmax, split_keys);
   if (n_split > 1) {
@@ -876,7 +950,10 @@ hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, c
     ca.n_split = n_split;
     ca.part = part;
     hipError_t e;
-    if (d == 128)
+    if (fuse)
+      e = launch_prefill_t<128, 4, false, true, false, true, true, (PLX_CHUNK_NT != 0), true>(
+          q, kc, vc, rho, gate, out, B, H, Lmax, sl2, s, {}, ca);
+    else if (d == 128)
       e = nt ? launch_chunk_t<128, true, true>(q, kc, vt, rho, gate, out, B, H, Lmax, sl2, s, ca)
              : launch_chunk_t<128, true, false>(q, kc, vt, rho, gate, out, B, H, Lmax, sl2, s, ca);
     else
@@ -892,6 +969,9 @@ hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, c
                          ca);
     return hipGetLastError();
   }
+  if (fuse)
+    return launch_prefill_t<128, 4, false, true, false, true, false, (PLX_CHUNK_NT != 0), true>(
+        q, kc, vc, rho, gate, out, B, H, Lmax, sl2, s, {}, ca);
   if (d == 128)
     return nt ? launch_chunk_t<128, false, true>(q, kc, vt, rho, gate, out, B, H, Lmax, sl2, s, ca)
               : launch_chunk_t<128, false, false>(q, kc, vt, rho, gate, out, B, H, Lmax, sl2, s, ca);

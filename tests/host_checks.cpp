@@ -194,13 +194,22 @@ void training_and_chunk_rejections() {
   const char* fc = "parallax_prefill_chunk";
   // 1 x 3 heads, 16-query chunks, 130 cache rows: no split when the split
   // covers the cache, else 3 splits of 64 keys for 8 query rows
-  check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 16, 128, 192) ==
+  check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 17, 128, 192) ==
             ((parallax_prefill_workspace_bytes(2, 3, 130, 128, PLX_BF16) + 255) & ~(size_t)255),
         "chunk workspace = V^T tiles of the cache without a split");
-  check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 16, 128, 64) ==
+  check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 17, 128, 64) ==
             ((parallax_prefill_workspace_bytes(2, 3, 130, 128, PLX_BF16) + 255) & ~(size_t)255) +
                 (size_t)8 * 3 * 3 * (2 * 128 + 4) * 4,
         "chunk workspace adds T*H*S records of 2d+4 floats");
+  // d = 128 chunks of at most 16 queries convert the V tiles in the kernel
+  check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 16, 128, 192) == 0,
+        "fused-V chunk workspace without a split");
+  check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 16, 128, 64) ==
+            (size_t)8 * 3 * 3 * (2 * 128 + 4) * 4,
+        "fused-V chunk workspace = the split records");
+  check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 16, 64, 192) ==
+            ((parallax_prefill_workspace_bytes(2, 3, 130, 64, PLX_BF16) + 255) & ~(size_t)255),
+        "d = 64 chunks stage V^T");
   check(parallax_prefill_chunk_vt_workspace_bytes(2, 3, 8, 130, 16, 128, 192) == 0,
         "chunk_vt workspace without a split");
   check(parallax_prefill_chunk_vt_workspace_bytes(2, 3, 8, 130, 16, 128, 64) ==
@@ -322,6 +331,10 @@ void no_device_failures() {
   expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8, 64,
                                 0.f, PLX_BF16, 0, nullptr, 0, nullptr), PLX_ENOMEM,
          "parallax_prefill_chunk", "chunk allocation failure");
+  // fused V at d = 128 without a split needs no workspace: straight to the launch
+  expect(parallax_prefill_chunk(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8,
+                                128, 0.f, PLX_BF16, 0, nullptr, 0, nullptr), PLX_EHIP,
+         "parallax_prefill_chunk", "fused-V chunk launch failure");
   expect(parallax_stage_v_rows(P(0), P(1), I(2), I(3), 1, 1, 8, 64, 8, 64, nullptr), PLX_EHIP,
          "parallax_stage_v_rows", "stage rows launch failure");
   expect(parallax_prefill_chunk_vt(P(0), P(1), P(2), P(3), F(4), F(5), I(6), I(7), 1, 1, 8, 64, 8,
