@@ -193,13 +193,13 @@ __device__ __forceinline__ void chunk_geometry(const ChunkArgs& ca, int b, int* 
 // offset by the chunk's cache position.  SPLIT (with VARLEN) walks only the key
 // tiles of one split and writes the unnormalised state of every row (m, l, c,
 // sum p v, sum p r v) to ca.part for chunk_combine_kernel.  NT loads the K and
-// V tiles with the non-temporal cache policy.  FUSEV (chunks of at most 16
-// queries, so wave 0 is the only one with queries; plain schedule) reads V
-// straight from the bf16 cache: each raw tile is staged in LDS like K, and the
-// other waves convert it to the fp16 V^T tile layout (the layout stage_v
-// writes, the same values) while wave 0 computes the tile's scores.
+// V tiles with the non-temporal cache policy.  FUSEV > 0 (chunks of at most
+// 16 * FUSEV queries, so only waves 0 .. FUSEV-1 have queries; plain schedule)
+// reads V straight from the bf16 cache: each raw tile is staged in LDS like K,
+// and the remaining waves convert it to the fp16 V^T tile layout (the layout
+// stage_v writes, the same values) while the busy waves compute its scores.
 template <int D, int NW, bool PIPE, bool CORR, bool SAVE, bool VARLEN, bool SPLIT, bool NT,
-          bool FUSEV>
+          int FUSEV>
 __global__ __launch_bounds__(64 * NW, CORR ? (D == 64 ? PLX_PF_MINW_D64 : PLX_PF_MINW_D128)
                                           : (D == 64 ? PLX_SM_MINW_D64 : PLX_SM_MINW_D128))
 void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -211,7 +211,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   static_assert(CORR || !SAVE, "the training statistics belong to the Parallax kernel");
   static_assert(!(SAVE && VARLEN), "the training statistics are for whole sequences");
   static_assert(!SPLIT || (VARLEN && CORR), "key splits are for the chunked prefill");
-  static_assert(!FUSEV || (VARLEN && !PIPE && NW > 1), "fused V conversion: chunks, plain");
+  static_assert(FUSEV == 0 || (VARLEN && !PIPE && 64 * (NW - FUSEV) >= (D / 8) * (PF_BC / 8)),
+                "fused V conversion: chunks, plain schedule, one 8 x 8 block per idle thread");
   using LY = PfLayout<D>;
   constexpr int PF_BR = 16 * NW;                         // queries per workgroup
   constexpr int PF_THREADS = 64 * NW;
@@ -219,7 +220,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   constexpr int FB = D / 16;                             // 16-feature output blocks
 
   // FUSEV: K and raw V double-buffered, one V^T tile
-  constexpr int SMEM = FUSEV ? 4 * LY::K_ELEMS + LY::V_ELEMS : 2 * LY::STAGE;
+  constexpr int SMEM = FUSEV > 0 ? 4 * LY::K_ELEMS + LY::V_ELEMS : 2 * LY::STAGE;
   __shared__ __align__(16) uint16_t smem[SMEM];
 
   const int tid = threadIdx.x;
@@ -271,8 +272,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     qbase = ((size_t)c0 * H + h) * D;
     qstride = (size_t)H * D;
     kh = k + (size_t)bh * ca.Lmax * D;
-    // staged V^T tiles; FUSEV: the raw bf16 cache rows of this head, like K
-    vth = FUSEV ? vt + (size_t)bh * ca.Lmax * D : vt + (size_t)bh * ca.n64max * (D * PF_BC);
+    // staged V^T tiles; FUSEV > 0: the raw bf16 cache rows of this head, like K
+    vth = FUSEV > 0 ? vt + (size_t)bh * ca.Lmax * D : vt + (size_t)bh * ca.n64max * (D * PF_BC);
   }
   const int n_k = pos0 + n_q;
 
@@ -368,7 +369,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   };
   const char* vbase = reinterpret_cast<const char*>(vth);
   auto load_v = [&](int kt, int buf) {
-    if constexpr (FUSEV) {
+    if constexpr (FUSEV > 0) {
       // raw bf16 rows of the cache, laid out like K
       const int rows = min(PF_BC, n_k - kt * PF_BC);
       const char* tile = vbase + (size_t)kt * PF_BC * D * 2;
@@ -473,7 +474,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // value products O^T += V^T P^T, A_r^T += V^T T^T of tile kt_.
   auto softmax_pv = [&](auto vbuf, f32x4 (&sa)[4], f32x4 (&ra)[4]) {
     const float m_use = m_run;
-    const uint16_t* vs = FUSEV ? smem + 4 * LY::K_ELEMS
+    const uint16_t* vs = FUSEV > 0 ? smem + 4 * LY::K_ELEMS
                                : smem + 2 * LY::K_ELEMS + (int)vbuf * LY::V_ELEMS;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -501,22 +502,31 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       }
     }
   };
-  // FUSEV: raw V tile `buf` (bf16, K's layout) -> the fp16 V^T tile, by waves
-  // 1 .. NW-1.  Chunk c of V^T row f holds keys vt_key_of_pos(8c .. 8c+7) of
-  // feature f, converted bf16 -> fp32 -> fp16 (RNE) as stage_v does.
+  // FUSEV: raw V tile `buf` (bf16, K's layout) -> the fp16 V^T tile, by the
+  // waves past the busy ones, one 8 x 8 block per thread: features
+  // 8 fc .. 8 fc + 7 (one 16-byte chunk of each raw row) of the keys
+  // vt_key_of_pos(8c .. 8c+7) that chunk c of the V^T rows holds.  16-byte LDS
+  // reads, a transpose in registers, bf16 -> fp32 -> fp16 (RNE) as stage_v
+  // converts, 16-byte LDS writes.
   auto convert_v = [&](int buf) {
     const uint16_t* raw = smem + 2 * LY::K_ELEMS + buf * LY::K_ELEMS;
     uint16_t* vtl = smem + 4 * LY::K_ELEMS;
-    for (int idx = tid - 64; idx < D * PF_BC / 8; idx += 64 * (NW - 1)) {
-      const int f = idx >> 3, c = idx & 7;
+    const int item = tid - 64 * FUSEV;
+    if (item >= (D / 8) * (PF_BC / 8)) return;
+    const int c = item & 7, fc = item >> 3;
+    u32x4 in[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      in[e] = *reinterpret_cast<const u32x4*>(raw + LY::k_off(vt_key_of_pos(8 * c + e), fc));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
       f16x8 o;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int key = vt_key_of_pos(8 * c + e);
-        const uint32_t bits = raw[LY::k_off(key, f >> 3) + (f & 7)];
-        o[e] = (_Float16)__uint_as_float(bits << 16);
+        const uint32_t w = in[e][j >> 1];
+        o[e] = (_Float16)__uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
       }
-      *reinterpret_cast<f16x8*>(vtl + LY::v_off(f, c)) = o;
+      *reinterpret_cast<f16x8*>(vtl + LY::v_off(8 * fc + j, c)) = o;
     }
   };
   // Pipelined step: the score MFMAs of tile kt_+1, the softmax and value MFMAs
@@ -573,7 +583,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         } else {
           softmax_pv(par, cs, cr);
         }
-      } else if constexpr (!FUSEV) {
+      } else if constexpr (FUSEV == 0) {
         scores(par, cs, cr);
         const float m_tile = needs_mask(kt) ? tile_max(cs, kt, std::true_type{})
                                             : tile_max(cs, kt, std::false_type{});
@@ -582,9 +592,9 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         softmax_pv(par, cs, cr);
       }
     }
-    if constexpr (FUSEV) {
-      // wave 0: the scores of tile kt; the other waves: its V^T tile
-      if (wave_u == 0) {
+    if constexpr (FUSEV > 0) {
+      // the busy waves: the scores of tile kt; the other waves: its V^T tile
+      if (wave_u < FUSEV) {
         if (kt < w_end) {
           scores(par, cs, cr);
           const float m_tile = needs_mask(kt) ? tile_max(cs, kt, std::true_type{})
@@ -758,7 +768,7 @@ struct TrainOut {
 };
 
 template <int D, int NW, bool PIPE, bool CORR, bool SAVE = false, bool VARLEN = false,
-          bool SPLIT = false, bool NT = false, bool FUSEV = false>
+          bool SPLIT = false, bool NT = false, int FUSEV = 0>
 static hipError_t launch_prefill_t(const void* q, const void* k, const void* vt,
                                    const void* rho, const float* gate, float* out, int B,
                                    int H, int L, float sl2, hipStream_t s, TrainOut tr = {},
@@ -906,8 +916,24 @@ size_t chunk_part_bytes(int T, int H, int Lmax, int d, int split_keys) {
 
 // Whether a per-call chunked prefill reads V straight from the bf16 cache and
 // converts its tiles in the kernel (no staging pass, no staged V^T workspace):
-// d = 128 with chunks of at most 16 queries, one busy wave per workgroup.
-bool chunk_fuses_v(int d, int max_q) { return PLX_CHUNK_FUSEV && d == 128 && max_q <= 16; }
+// d = 128 with chunks of at most 32 queries, at most two busy waves of four.
+bool chunk_fuses_v(int d, int max_q) { return PLX_CHUNK_FUSEV && d == 128 && max_q <= 32; }
+
+// The fused-V chunk kernel (d = 128, four waves, plain schedule, non-temporal
+// tile loads: a chunk of at most 32 queries is one query tile, so no workgroup
+// re-reads a tile): the waves holding queries (one for chunks of at most 16,
+// else two) compute, the others convert the V tiles.
+template <bool SPLIT>
+static hipError_t launch_fused_t(int max_q, const void* q, const void* kc, const void* vc,
+                                 const void* rho, const float* gate, float* out, int B, int H,
+                                 int Lmax, float sl2, hipStream_t s, const ChunkArgs& ca) {
+  constexpr bool NT = PLX_CHUNK_NT != 0;
+  if (max_q <= 16)
+    return launch_prefill_t<128, 4, false, true, false, true, SPLIT, NT, 1>(
+        q, kc, vc, rho, gate, out, B, H, Lmax, sl2, s, {}, ca);
+  return launch_prefill_t<128, 4, false, true, false, true, SPLIT, NT, 2>(
+      q, kc, vc, rho, gate, out, B, H, Lmax, sl2, s, {}, ca);
+}
 
 // The chunked-prefill kernel at head dimension D (split-KV or not, NT cache policy).
 template <int D, bool SPLIT, bool NT>
@@ -931,8 +957,8 @@ hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, c
   const float sl2 = scale * kLog2e;
   const int n64 = (Lmax + PF_BC - 1) / PF_BC;
   ChunkArgs ca{cu_q, ctx, T, Lmax, max_q, n64, 0};
-  // Per-call V at d = 128 with one-wave chunks: the kernel converts the raw V
-  // tiles itself (no staging pass, and vt is not used).
+  // Per-call V at d = 128 with chunks of at most 32 queries: the kernel
+  // converts the raw V tiles itself (no staging pass, and vt is not used).
   const bool fuse = vc != nullptr && chunk_fuses_v(d, max_q);
   if (vc && !fuse) {
     hipError_t e = launch_stage_v_rows(vc, vt, cu_q, ctx, B, H, T, Lmax, max_q, d, false, s);
@@ -951,8 +977,7 @@ hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, c
     ca.part = part;
     hipError_t e;
     if (fuse)
-      e = launch_prefill_t<128, 4, false, true, false, true, true, (PLX_CHUNK_NT != 0), true>(
-          q, kc, vc, rho, gate, out, B, H, Lmax, sl2, s, {}, ca);
+      e = launch_fused_t<true>(max_q, q, kc, vc, rho, gate, out, B, H, Lmax, sl2, s, ca);
     else if (d == 128)
       e = nt ? launch_chunk_t<128, true, true>(q, kc, vt, rho, gate, out, B, H, Lmax, sl2, s, ca)
              : launch_chunk_t<128, true, false>(q, kc, vt, rho, gate, out, B, H, Lmax, sl2, s, ca);
@@ -969,9 +994,7 @@ hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, c
                          ca);
     return hipGetLastError();
   }
-  if (fuse)
-    return launch_prefill_t<128, 4, false, true, false, true, false, (PLX_CHUNK_NT != 0), true>(
-        q, kc, vc, rho, gate, out, B, H, Lmax, sl2, s, {}, ca);
+  if (fuse) return launch_fused_t<false>(max_q, q, kc, vc, rho, gate, out, B, H, Lmax, sl2, s, ca);
   if (d == 128)
     return nt ? launch_chunk_t<128, false, true>(q, kc, vt, rho, gate, out, B, H, Lmax, sl2, s, ca)
               : launch_chunk_t<128, false, false>(q, kc, vt, rho, gate, out, B, H, Lmax, sl2, s, ca);

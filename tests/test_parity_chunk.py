@@ -40,6 +40,8 @@ CASES = [  # (ctx per sequence, chunk length per sequence)
     ([60, 4, 0, 130], [16, 17, 15, 64]),
     ([1000, 7], [65, 200]),
     ([100, 0, 33, 257, 5], [33, 1, 128, 9, 300]),
+    ([60, 4, 0, 130], [16, 17, 15, 32]),               # 17-32 queries: two busy waves
+    ([0, 191, 64], [32, 18, 29]),
 ]
 
 
@@ -198,6 +200,8 @@ SPLIT_CASES = [  # (ctx per sequence, chunk length per sequence, keys per split)
     ([100, 0, 33, 257, 5], [33, 1, 128, 9, 300], 192),
     ([3000], [16], 0),                                 # the library's split
     ([5000, 20], [1, 130], 0),
+    ([60, 4, 0, 130], [16, 17, 15, 32], 64),
+    ([2500, 1000], [32, 20], 0),
 ]
 
 
@@ -270,5 +274,32 @@ def test_chunk_random_shapes(seed):
     torch.cuda.synchronize()
     print(f"random {seed}: B{B} H{H} d{d} ctx{ctx} n{n} split {split}: max-abs {err:.3e}",
           flush=True)
+    assert err <= TOL
+    assert torch.equal(staged, out)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_chunk_random_short_chunks(seed):
+    """Seeded random batches of short chunks at d = 128 (1-32 queries, the shapes
+    whose per-call V tiles the kernel converts itself): 1-8 sequences, 0-3000
+    cached keys, the library's split, an explicit split or none.  Every row
+    against the oracle; the staged-cache call gives the same bits."""
+    plx = _plx()
+    rng = np.random.default_rng(2100 + seed)
+    B = int(rng.integers(1, 9))
+    ctx = [int(x) for x in rng.integers(0, 3001, B)]
+    n = [int(x) for x in rng.integers(1, 17 if seed % 2 else 33, B)]
+    H = int(rng.integers(1, 5))
+    inp = wl.chunk_inputs(H, 128, ctx, n, seed=2200 + seed, device="cuda", rho_std=0.5)
+    Lmax = inp["kcache"].shape[2]
+    split = [0, 64 * int(rng.integers(1, 9)), (Lmax + 63) // 64 * 64][seed % 3]
+    out = _run(inp, split_keys=split)
+    err = float(np.max(np.abs(out.cpu().double().numpy() - _oracle(inp))))
+    vt = plx.prefill_stage_v(inp["vcache"])
+    staged = plx.prefill_chunk(inp["q"], inp["kcache"], None, inp["rho"], inp["gate"],
+                               inp["cu_q"], inp["ctx"], inp["max_q"], vt_cache=vt,
+                               split_keys=split)
+    torch.cuda.synchronize()
+    print(f"short {seed}: B{B} H{H} ctx{ctx} n{n} split {split}: max-abs {err:.3e}", flush=True)
     assert err <= TOL
     assert torch.equal(staged, out)
