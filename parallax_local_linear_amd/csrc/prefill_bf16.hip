@@ -93,7 +93,7 @@ constexpr int kWaitLgkm0 = 0xC07F;
 #ifndef PLX_CHUNK_NT
 #define PLX_CHUNK_NT 1
 #endif
-// Per-call chunked prefill at d = 128 with at most 16 queries per chunk: convert
+// Per-call chunked prefill at d = 128 with at most 32 queries per chunk: convert
 // the raw V tiles in the kernel (1) instead of a staging pass (0).
 #ifndef PLX_CHUNK_FUSEV
 #define PLX_CHUNK_FUSEV 1
@@ -916,7 +916,9 @@ size_t chunk_part_bytes(int T, int H, int Lmax, int d, int split_keys) {
 
 // Whether a per-call chunked prefill reads V straight from the bf16 cache and
 // converts its tiles in the kernel (no staging pass, no staged V^T workspace):
-// d = 128 with chunks of at most 32 queries, at most two busy waves of four.
+// d = 128 with chunks of at most 32 queries.  A tile is 128 blocks of 8 x 8, one
+// per converting thread, so two of the four waves convert.  (At d = 64 the
+// kernel's 128-register budget spills in this form; it keeps the staging pass.)
 bool chunk_fuses_v(int d, int max_q) { return PLX_CHUNK_FUSEV && d == 128 && max_q <= 32; }
 
 // The fused-V chunk kernel (d = 128, four waves, plain schedule, non-temporal
@@ -957,8 +959,8 @@ hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, c
   const float sl2 = scale * kLog2e;
   const int n64 = (Lmax + PF_BC - 1) / PF_BC;
   ChunkArgs ca{cu_q, ctx, T, Lmax, max_q, n64, 0};
-  // Per-call V at d = 128 with chunks of at most 32 queries: the kernel
-  // converts the raw V tiles itself (no staging pass, and vt is not used).
+  // Per-call V with short chunks: the kernel converts the raw V tiles itself
+  // (no staging pass, and vt is not used).
   const bool fuse = vc != nullptr && chunk_fuses_v(d, max_q);
   if (vc && !fuse) {
     hipError_t e = launch_stage_v_rows(vc, vt, cu_q, ctx, B, H, T, Lmax, max_q, d, false, s);
@@ -994,7 +996,8 @@ hipError_t launch_prefill_chunk(const void* q, const void* kc, const void* vc, c
                          ca);
     return hipGetLastError();
   }
-  if (fuse) return launch_fused_t<false>(max_q, q, kc, vc, rho, gate, out, B, H, Lmax, sl2, s, ca);
+  if (fuse)
+    return launch_fused_t<false>(max_q, q, kc, vc, rho, gate, out, B, H, Lmax, sl2, s, ca);
   if (d == 128)
     return nt ? launch_chunk_t<128, false, true>(q, kc, vt, rho, gate, out, B, H, Lmax, sl2, s, ca)
               : launch_chunk_t<128, false, false>(q, kc, vt, rho, gate, out, B, H, Lmax, sl2, s, ca);
