@@ -689,20 +689,23 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 template <int D, typename TOUT, bool VARLEN = false>
 __global__ __launch_bounds__(256)
 void stage_v_kernel(const __bf16* __restrict__ v, TOUT* __restrict__ vt, int L, int n_kt,
-                    ChunkArgs ca = {}, int H = 1) {
+                    ChunkArgs ca = {}, int H = 1, int span = 0) {
   typedef TOUT outx8 __attribute__((ext_vector_type(8)));
   constexpr int PITCH = D + 2;     // odd dword pitch spreads the column reads over banks
   __shared__ uint16_t tile[PF_BC * PITCH];
-  const int bh = blockIdx.x / n_kt;
-  const int kt = blockIdx.x % n_kt;
+  // workgroups per head: every tile, or (new rows only) the `span` tiles from
+  // the one holding the chunk's first row
+  const int per = (VARLEN && ca.new_rows_only) ? span : n_kt;
+  const int bh = blockIdx.x / per;
+  int kt = blockIdx.x % per;
   const int tid = threadIdx.x;
   int n_valid = L;                      // rows of this head that exist
   if constexpr (VARLEN) {
     int c0, n_q, pos0;
     chunk_geometry(ca, bh / H, &c0, &n_q, &pos0);
     n_valid = pos0 + n_q;
+    if (ca.new_rows_only) kt += pos0 / PF_BC;
     if (kt * PF_BC >= n_valid) return;  // uniform over the workgroup
-    if (ca.new_rows_only && kt < pos0 / PF_BC) return;
   }
   const __bf16* src = v + ((size_t)bh * L + (size_t)kt * PF_BC) * D;
   constexpr int CH = PF_BC * D / 8;
@@ -812,13 +815,17 @@ hipError_t launch_stage_v_rows(const void* vc, void* vt, const int* cu_q, const 
                                hipStream_t s) {
   const int n64 = (Lmax + PF_BC - 1) / PF_BC;
   const ChunkArgs ca{cu_q, ctx, T, Lmax, max_q, n64, new_rows_only ? 1 : 0};
-  const dim3 grid((unsigned)(B * H * n64));
+  // new rows only: a chunk of n <= min(max_q, Lmax) rows spans at most
+  // floor((n + 62) / 64) + 1 tiles, so the grid covers only those of each head
+  const int mq = min(max_q, Lmax);
+  const int span = new_rows_only ? min(n64, (mq + PF_BC - 2) / PF_BC + 1) : n64;
+  const dim3 grid((unsigned)(B * H * span));
   if (d == 128)
     hipLaunchKernelGGL((stage_v_kernel<128, _Float16, true>), grid, dim3(256), 0, s,
-                       (const __bf16*)vc, (_Float16*)vt, Lmax, n64, ca, H);
+                       (const __bf16*)vc, (_Float16*)vt, Lmax, n64, ca, H, span);
   else
     hipLaunchKernelGGL((stage_v_kernel<64, _Float16, true>), grid, dim3(256), 0, s,
-                       (const __bf16*)vc, (_Float16*)vt, Lmax, n64, ca, H);
+                       (const __bf16*)vc, (_Float16*)vt, Lmax, n64, ca, H, span);
   return hipGetLastError();
 }
 
