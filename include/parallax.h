@@ -179,7 +179,7 @@ int parallax_decode_default_split(int B, int H, int Lmax, int d);
  * `stream` when it needs any) holds the fp16 V^T tiles of the cache rows the
  * chunks read and, when split, the partial states (T*H*S records of 2d+4
  * floats, S = ceil(ceil(Lmax/64) / (split_keys/64))).  At d = 128 with
- * max_q <= 32 the kernel converts the bf16 V tiles itself, so there are no
+ * max_q <= 64 the kernel converts the bf16 V tiles itself, so there are no
  * V^T tiles and, without a split, the size is 0. */
 size_t parallax_prefill_chunk_workspace_bytes(int B, int H, int T, int Lmax, int max_q, int d,
                                               int split_keys);

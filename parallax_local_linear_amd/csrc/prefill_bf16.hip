@@ -93,8 +93,9 @@ constexpr int kWaitLgkm0 = 0xC07F;
 #ifndef PLX_CHUNK_NT
 #define PLX_CHUNK_NT 1
 #endif
-// Per-call chunked prefill at d = 128 with at most 32 queries per chunk: convert
-// the raw V tiles in the kernel (1) instead of a staging pass (0).
+// Per-call chunked prefill at d = 128 with at most 64 queries per chunk (one
+// query tile): convert the raw V tiles in the kernel (1) instead of a staging
+// pass (0).
 #ifndef PLX_CHUNK_FUSEV
 #define PLX_CHUNK_FUSEV 1
 #endif
@@ -211,8 +212,11 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   static_assert(CORR || !SAVE, "the training statistics belong to the Parallax kernel");
   static_assert(!(SAVE && VARLEN), "the training statistics are for whole sequences");
   static_assert(!SPLIT || (VARLEN && CORR), "key splits are for the chunked prefill");
-  static_assert(FUSEV == 0 || (VARLEN && !PIPE && 64 * (NW - FUSEV) >= (D / 8) * (PF_BC / 8)),
-                "fused V conversion: chunks, plain schedule, one 8 x 8 block per idle thread");
+  static_assert(FUSEV == 0 || (VARLEN && !PIPE &&
+                               (FUSEV == NW ? 64 * NW >= 2 * (D / 8) * (PF_BC / 8)
+                                            : 64 * (NW - FUSEV) >= (D / 8) * (PF_BC / 8))),
+                "fused V conversion: chunks, plain schedule, a converting thread per block "
+                "(per half block when every wave is busy)");
   using LY = PfLayout<D>;
   constexpr int PF_BR = 16 * NW;                         // queries per workgroup
   constexpr int PF_THREADS = 64 * NW;
@@ -502,31 +506,36 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       }
     }
   };
-  // FUSEV: raw V tile `buf` (bf16, K's layout) -> the fp16 V^T tile, by the
-  // waves past the busy ones, one 8 x 8 block per thread: features
-  // 8 fc .. 8 fc + 7 (one 16-byte chunk of each raw row) of the keys
-  // vt_key_of_pos(8c .. 8c+7) that chunk c of the V^T rows holds.  16-byte LDS
-  // reads, a transpose in registers, bf16 -> fp32 -> fp16 (RNE) as stage_v
-  // converts, 16-byte LDS writes.
+  // FUSEV: raw V tile `buf` (bf16, K's layout) -> the fp16 V^T tile, in 8 x 8
+  // blocks: features 8 fc .. 8 fc + 7 (one 16-byte chunk of each raw row) of
+  // the keys vt_key_of_pos(8c .. 8c+7) that chunk c of the V^T rows holds.
+  // 16-byte LDS reads, a transpose in registers, bf16 -> fp32 -> fp16 (RNE) as
+  // stage_v converts, 16- (or 8-) byte LDS writes.  The waves past the busy
+  // ones take a block per thread; when every wave is busy, all threads take
+  // half a block (4 of the 8 keys) each.
   auto convert_v = [&](int buf) {
+    constexpr bool ALL = FUSEV == NW;
+    constexpr int KP = ALL ? 4 : 8;                      // keys per thread
+    typedef _Float16 f16xkp __attribute__((ext_vector_type(KP)));
     const uint16_t* raw = smem + 2 * LY::K_ELEMS + buf * LY::K_ELEMS;
     uint16_t* vtl = smem + 4 * LY::K_ELEMS;
-    const int item = tid - 64 * FUSEV;
+    const int item = ALL ? tid >> 1 : tid - 64 * FUSEV;
+    const int e0 = ALL ? 4 * (tid & 1) : 0;
     if (item >= (D / 8) * (PF_BC / 8)) return;
     const int c = item & 7, fc = item >> 3;
-    u32x4 in[8];
+    u32x4 in[KP];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      in[e] = *reinterpret_cast<const u32x4*>(raw + LY::k_off(vt_key_of_pos(8 * c + e), fc));
+    for (int e = 0; e < KP; ++e)
+      in[e] = *reinterpret_cast<const u32x4*>(raw + LY::k_off(vt_key_of_pos(8 * c + e0 + e), fc));
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      f16x8 o;
+      f16xkp o;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < KP; ++e) {
         const uint32_t w = in[e][j >> 1];
         o[e] = (_Float16)__uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
       }
-      *reinterpret_cast<f16x8*>(vtl + LY::v_off(8 * fc + j, c)) = o;
+      *reinterpret_cast<f16xkp*>(vtl + LY::v_off(8 * fc + j, c) + e0) = o;
     }
   };
   // Pipelined step: the score MFMAs of tile kt_+1, the softmax and value MFMAs
@@ -594,6 +603,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     }
     if constexpr (FUSEV > 0) {
       // the busy waves: the scores of tile kt; the other waves: its V^T tile
+      // (every wave busy: each converts its share first, then its scores)
+      if constexpr (FUSEV == NW) convert_v(P);
       if (wave_u < FUSEV) {
         if (kt < w_end) {
           scores(par, cs, cr);
@@ -602,7 +613,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
           if (kt == t_beg) m_run = m_tile;      // accumulators are still zero
           rescale_to(m_tile);
         }
-      } else {
+      } else if constexpr (FUSEV < NW) {
         convert_v(P);
       }
       // V^T complete: this wave's LDS writes are done (lgkmcnt); a bare barrier,
@@ -923,15 +934,16 @@ size_t chunk_part_bytes(int T, int H, int Lmax, int d, int split_keys) {
 
 // Whether a per-call chunked prefill reads V straight from the bf16 cache and
 // converts its tiles in the kernel (no staging pass, no staged V^T workspace):
-// d = 128 with chunks of at most 32 queries.  A tile is 128 blocks of 8 x 8, one
-// per converting thread, so two of the four waves convert.  (At d = 64 the
+// d = 128 with chunks of at most 64 queries, one query tile.  (At d = 64 the
 // kernel's 128-register budget spills in this form; it keeps the staging pass.)
-bool chunk_fuses_v(int d, int max_q) { return PLX_CHUNK_FUSEV && d == 128 && max_q <= 32; }
+bool chunk_fuses_v(int d, int max_q) { return PLX_CHUNK_FUSEV && d == 128 && max_q <= 64; }
 
 // The fused-V chunk kernel (d = 128, four waves, plain schedule, non-temporal
-// tile loads: a chunk of at most 32 queries is one query tile, so no workgroup
-// re-reads a tile): the waves holding queries (one for chunks of at most 16,
-// else two) compute, the others convert the V tiles.
+// tile loads: a chunk of at most 64 queries is one query tile, so no workgroup
+// re-reads a tile).  A tile is 128 blocks of 8 x 8.  Chunks of at most 16
+// queries: wave 0 computes while waves 1-2 convert a block per thread; at most
+// 32: waves 0-1 compute, waves 2-3 convert; else every wave converts half a
+// block per thread and then computes.
 template <bool SPLIT>
 static hipError_t launch_fused_t(int max_q, const void* q, const void* kc, const void* vc,
                                  const void* rho, const float* gate, float* out, int B, int H,
@@ -940,7 +952,10 @@ static hipError_t launch_fused_t(int max_q, const void* q, const void* kc, const
   if (max_q <= 16)
     return launch_prefill_t<128, 4, false, true, false, true, SPLIT, NT, 1>(
         q, kc, vc, rho, gate, out, B, H, Lmax, sl2, s, {}, ca);
-  return launch_prefill_t<128, 4, false, true, false, true, SPLIT, NT, 2>(
+  if (max_q <= 32)
+    return launch_prefill_t<128, 4, false, true, false, true, SPLIT, NT, 2>(
+        q, kc, vc, rho, gate, out, B, H, Lmax, sl2, s, {}, ca);
+  return launch_prefill_t<128, 4, false, true, false, true, SPLIT, NT, 4>(
       q, kc, vc, rho, gate, out, B, H, Lmax, sl2, s, {}, ca);
 }
 

@@ -194,18 +194,20 @@ void training_and_chunk_rejections() {
   const char* fc = "parallax_prefill_chunk";
   // 1 x 3 heads, 16-query chunks, 130 cache rows: no split when the split
   // covers the cache, else 3 splits of 64 keys for 8 query rows
-  check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 33, 128, 192) ==
+  check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 65, 128, 192) ==
             ((parallax_prefill_workspace_bytes(2, 3, 130, 128, PLX_BF16) + 255) & ~(size_t)255),
         "chunk workspace = V^T tiles of the cache without a split");
-  check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 33, 128, 64) ==
+  check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 65, 128, 64) ==
             ((parallax_prefill_workspace_bytes(2, 3, 130, 128, PLX_BF16) + 255) & ~(size_t)255) +
                 (size_t)8 * 3 * 3 * (2 * 128 + 4) * 4,
         "chunk workspace adds T*H*S records of 2d+4 floats");
-  // d = 128 chunks of at most 32 queries convert the V tiles in the kernel
+  // d = 128 chunks of at most 64 queries convert the V tiles in the kernel
   check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 16, 128, 192) == 0,
         "fused-V chunk workspace without a split");
   check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 32, 128, 192) == 0,
         "fused-V chunk workspace with two busy waves");
+  check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 64, 128, 192) == 0,
+        "fused-V chunk workspace with four busy waves");
   check(parallax_prefill_chunk_workspace_bytes(2, 3, 8, 130, 16, 128, 64) ==
             (size_t)8 * 3 * 3 * (2 * 128 + 4) * 4,
         "fused-V chunk workspace = the split records");

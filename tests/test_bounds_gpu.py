@@ -199,14 +199,15 @@ def test_training_writes_stay_in_bounds(d):
 
 
 @pytest.mark.parametrize("ctx,n", [([70, 0, 5], [20, 90, 1]), ([70, 0, 130], [16, 9, 1]),
-                                   ([70, 0, 130], [16, 9, 30])],
-                         ids=["staged", "fused1", "fused2"])
+                                   ([70, 0, 130], [16, 9, 30]), ([70, 0, 130], [40, 9, 64])],
+                         ids=["staged", "fused1", "fused2", "fused4"])
 @pytest.mark.parametrize("split", [0, 64])
 def test_chunk_writes_stay_in_bounds(split, ctx, n):
     """Per-call call and the staged-cache call, whole-prefix (split 0 is no
     split at this size) and split-KV (4 splits of 64 keys).  Chunks of up to 90
-    queries stage V^T per call; chunks of at most 32 queries at d = 128 convert
-    the V tiles in the kernel (no V^T workspace), with one or two busy waves."""
+    queries stage V^T per call; chunks of at most 64 queries at d = 128 convert
+    the V tiles in the kernel (no V^T workspace), with one, two or four busy
+    waves."""
     lib = _native.lib()
     stream = torch.cuda.current_stream().cuda_stream
     H, d = 2, 128
@@ -215,7 +216,7 @@ def test_chunk_writes_stay_in_bounds(split, ctx, n):
     T = inp["T"]
     ob, op = _guarded(T * H * d * 4)
     ws = lib.parallax_prefill_chunk_workspace_bytes(3, H, T, 200, inp["max_q"], d, split)
-    assert (ws == 0) == (inp["max_q"] <= 32 and split == 0)
+    assert (ws == 0) == (inp["max_q"] <= 64 and split == 0)
     ws = max(ws, 256)
     wb, wp = _guarded(ws)
     st = lib.parallax_prefill_chunk(inp["q"].data_ptr(), inp["kcache"].data_ptr(),

@@ -280,7 +280,7 @@ def test_chunk_random_shapes(seed):
 
 @pytest.mark.parametrize("seed", range(8))
 def test_chunk_random_short_chunks(seed):
-    """Seeded random batches of short chunks at d = 128 (1-32 queries, the shapes
+    """Seeded random batches of short chunks at d = 128 (1-64 queries, the shapes
     whose per-call V tiles the kernel converts itself): 1-8 sequences, 0-3000
     cached keys, the library's split, an explicit split or none.  Every row
     against the oracle; the staged-cache call gives the same bits."""
@@ -288,7 +288,7 @@ def test_chunk_random_short_chunks(seed):
     rng = np.random.default_rng(2100 + seed)
     B = int(rng.integers(1, 9))
     ctx = [int(x) for x in rng.integers(0, 3001, B)]
-    n = [int(x) for x in rng.integers(1, 17 if seed % 2 else 33, B)]
+    n = [int(x) for x in rng.integers(1, (17, 33, 65)[seed % 3], B)]
     H = int(rng.integers(1, 5))
     inp = wl.chunk_inputs(H, 128, ctx, n, seed=2200 + seed, device="cuda", rho_std=0.5)
     Lmax = inp["kcache"].shape[2]
