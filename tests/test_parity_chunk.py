@@ -74,8 +74,11 @@ def test_empty_cache_chunk_is_the_prefill(d):
     assert torch.equal(out, ref[0].transpose(0, 1))
 
 
-def test_cache_past_the_chunk_is_never_read_and_other_rows_untouched():
-    ctx, n = [50, 200, 3], [20, 70, 100]
+@pytest.mark.parametrize("n", [[20, 70, 100], [20, 7, 64]], ids=["staged", "fused"])
+def test_cache_past_the_chunk_is_never_read_and_other_rows_untouched(n):
+    """NaN in every cache row past each chunk changes no output bit.  Chunks of at
+    most 64 queries at d = 128 read V straight from the cache (fused path)."""
+    ctx = [50, 200, 3]
     inp = wl.chunk_inputs(2, 128, ctx, n, seed=1310, device="cuda", Lmax=400)
     a = _run(inp).clone()
     for b in range(3):
