@@ -151,7 +151,7 @@ def test_staged_cache_matches_per_call_staging(case, d):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_incremental_serving_with_a_staged_cache(d):
-    """Three rounds of appended chunks: the new K/V rows are written into the
+    """Four rounds of appended chunks: the new K/V rows are written into the
     caches (whose unwritten rows hold NaN), stage_v_rows re-stages only their
     tiles, and the chunk reads the staged cache.  Every round matches the
     oracle and the per-call-staging path bit for bit."""
@@ -170,7 +170,7 @@ def test_incremental_serving_with_a_staged_cache(d):
     cu0 = torch.tensor([0] + list(np.cumsum(ctx)), dtype=torch.int32, device="cuda")
     zero = torch.zeros(B, dtype=torch.int32, device="cuda")
     plx.stage_v_rows(vc, vt, cu0, zero, max(ctx), int(sum(ctx)))
-    for n in ([5, 64, 17], [1, 1, 80], [70, 3, 0]):
+    for n in ([5, 64, 17], [1, 1, 80], [70, 3, 0], [16, 1, 9]):
         for b in range(B):
             kc[b, :, ctx[b]:ctx[b] + n[b]] = torch.randn((H, n[b], d), generator=g,
                                                         device="cuda").to(torch.bfloat16)
