@@ -29,7 +29,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 def _real_impl():
     return types.SimpleNamespace(prefill=po.prefill, decode=po.decode,
                                  explicit_row=po.explicit_row,
-                                 prefill_explicit=po.prefill_explicit)
+                                 prefill_explicit=po.prefill_explicit,
+                                 prefill_rows=po.prefill_rows)
 
 
 def _rand(rng, *shape, std=1.0):
@@ -243,9 +244,42 @@ def pin_decode_matches_prefill_row(impl):
         np.testing.assert_allclose(dec, pre[:, :, i], rtol=0, atol=1e-12)
 
 
+def pin_prefill_rows(impl):
+    """The selected-rows checker (explicit form, one head at a time) against the
+    score-tilt derivative of torch's fp64 causal SDPA (the independent reference
+    of pin_correction_is_score_tilt_derivative), at rows 0, 1, a middle row and
+    the last row of every head of a B=2, H=3 case whose heads have distinct
+    gates; and against the expanded form on the same rows."""
+    c = _prefill_case(16, B=2, H=3, L=21, dk=6, dv=5, rho_std=1.3)
+    c["gate"] = np.array([0.25, 0.6, 1.1])
+    sc = 0.47
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    q, k, v, rho = map(t, (c["q"], c["k"], c["v"], c["rho"]))
+
+    def att(x):
+        return F.scaled_dot_product_attention(x, k, v, is_causal=True, scale=sc)
+
+    o_sa, dd = torch.func.jvp(att, (q,), (rho / sc,))
+    ref = (o_sa - torch.from_numpy(c["gate"])[None, :, None, None] * dd).numpy()
+    full = impl.prefill(c["q"], c["k"], c["v"], c["rho"], c["gate"], scale=sc)
+    rows = [0, 1, 10, 20]
+    for b in range(2):
+        for h in range(3):
+            got = impl.prefill_rows(c["q"], c["k"], c["v"], c["rho"], c["gate"], b, h, rows,
+                                    scale=sc)
+            assert got.shape == (len(rows), 5)
+            np.testing.assert_allclose(got, ref[b, h, rows], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(got, full[b, h, rows], rtol=0, atol=1e-12)
+    # the default scale is 1/sqrt(d_k)
+    got = impl.prefill_rows(c["q"], c["k"], c["v"], c["rho"], c["gate"], 1, 2, [20])
+    full = impl.prefill(c["q"], c["k"], c["v"], c["rho"], c["gate"], scale=1 / np.sqrt(6))
+    np.testing.assert_allclose(got[0], full[1, 2, 20], rtol=0, atol=1e-12)
+
+
 PINS = [pin_rho_zero_is_softmax_attention, pin_sigma_is_weighted_covariance,
         pin_correction_is_score_tilt_derivative, pin_local_linear_regression,
-        pin_closed_forms, pin_invariants, pin_hand_cases, pin_decode_matches_prefill_row]
+        pin_closed_forms, pin_invariants, pin_hand_cases, pin_decode_matches_prefill_row,
+        pin_prefill_rows]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -356,14 +390,39 @@ def _mutant_decode(prefill_impl):
     return decode
 
 
+def _mutant_prefill_rows(kind):
+    """prefill_rows with one plausible indexing mistake."""
+    def prefill_rows(q, k, v, rho, gate, b, h, rows, scale=None):
+        dk = q.shape[-1]
+        sc = 1 / np.sqrt(dk) if scale is None else scale
+        gf = po._f64(gate)
+        g = float(gf[b] if kind == "rows_gate_by_b" else gf[h])
+        res = []
+        for i in rows:
+            i = int(i)
+            n = i if kind == "rows_diagonal_dropped" else i + 1
+            if kind == "rows_key_window_shifted":
+                K, V = k[b, h, 1: i + 2], v[b, h, 1: i + 2]
+            else:
+                K, V = k[b, h, : max(n, 1)], v[b, h, : max(n, 1)]
+            qi = q[b, h, i]
+            ri = rho[b, h, i - 1] if kind == "rows_rho_of_previous_row" else rho[b, h, i]
+            res.append(po.explicit_row(qi, K, V, ri, g, sc)[0])
+        return np.stack(res)
+    return prefill_rows
+
+
 MUTANTS = ["sign_flip", "dropped_mean_term", "scaled_r", "mask_off_by_one",
-           "gate_on_output", "uncentred", "transposed"]
+           "gate_on_output", "uncentred", "transposed", "rows_diagonal_dropped",
+           "rows_gate_by_b", "rows_key_window_shifted", "rows_rho_of_previous_row"]
 
 
 @pytest.mark.parametrize("kind", MUTANTS)
 def test_planted_mistakes_are_caught(kind):
     impl = _real_impl()
-    if kind in ("uncentred", "transposed"):
+    if kind.startswith("rows_"):
+        impl.prefill_rows = _mutant_prefill_rows(kind)
+    elif kind in ("uncentred", "transposed"):
         impl.explicit_row = _mutant_explicit_row(kind)
     else:
         impl.prefill = _mutant_prefill(kind)
