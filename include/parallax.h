@@ -74,11 +74,18 @@ const char* parallax_last_error(void);
  * bytes (0 for PLX_F32).  If workspace is NULL the library allocates and frees
  * it on `stream` (stream-ordered allocation).  In PLX_BF16 mode the workspace
  * holds V converted to fp16 in a per-64-key-tile transposed layout (see
- * parallax_prefill_stage_v); the conversion is exact for |v| in
- * [2^-14, 65504] and values must stay below 65504 in magnitude.  The bf16 path
- * rounds the softmax numerators P (kept <= 16) and <rho,k_j> to fp16 and forms
- * T = P*<rho,k_j> in fp16 for the value products, so |<rho,k_j>| must stay
- * below 4094. */
+ * parallax_prefill_stage_v).  Range of the bf16 path:
+ *   - V: fp16 holds every bf16 value with |v| <= 65280 exactly (subnormal fp16
+ *     below 2^-14, absolute error < 2^-25).  fp16 cannot represent larger
+ *     magnitudes: they are clamped to +-65504, so a row that attends such a
+ *     value gets the clamped value, while rows that do not attend it are
+ *     unaffected (in particular, never NaN).  |v| <= 65280 is the exact range.
+ *   - rho: no limit.  The softmax numerators P (kept <= 16) and
+ *     r_ij = <rho_i,k_j> are rounded to fp16 and T = P*r is formed in fp16 for
+ *     the value products; a row whose |r_ij| exceeds 2048 is scaled by a power
+ *     of two before that rounding and unscaled in fp32 at the end, which is
+ *     exact because Eq. 2 is linear in rho.  (Only an element of rho_i whose
+ *     magnitude falls below 2^-126 after that scaling loses bits.) */
 size_t parallax_prefill_workspace_bytes(int B, int H, int L, int d, int dtype);
 
 int parallax_prefill(const void* q, const void* k, const void* v, const void* rho,

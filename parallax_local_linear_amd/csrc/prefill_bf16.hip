@@ -122,9 +122,13 @@ constexpr int kWaitLgkm0 = 0xC07F;
 #define PLX_SM_MINW_D64 PLX_PF_MINW_D64
 #endif
 // Rescale slack in log2 units: P = 2^(s - m) may grow to 2^kRescaleSlack before
-// the running max m is moved.  Keeps fp16 P <= 16 and T = P*R within fp16 range
-// for |<rho,k>| < 4094.
+// the running max m is moved, so fp16 P <= 16.
 constexpr float kRescaleSlack = 4.0f;
+// Largest |R| a row may feed to the fp16 products: with P <= 16, T = P*R stays
+// below 2^15, inside fp16's range.  A row whose R exceeds it is scaled by a
+// power of two (exactly; Eq. 2 is linear in rho), see rescale_r.
+constexpr float kRMax = 2048.0f;
+static_assert(16.0f * kRMax < 65504.0f, "T = P*R must fit fp16");
 
 // LDS tiles have no padding; 16-byte chunks are XOR-swizzled by row instead,
 // which keeps every fragment read and tile store free of bank conflicts
@@ -144,6 +148,15 @@ struct PfLayout {
     return r * PF_BC + ((c ^ (r & 7)) << 3);
   }
 };
+
+// V goes to the fp16 value products through this: fp16 holds |v| <= 65504
+// exactly (bf16 values up to 65280), and larger magnitudes, which fp16 cannot
+// represent, are clamped to +-65504 instead of becoming infinite, so that a key
+// a row never attends (a masked key in its diagonal tile, P = 0) cannot turn
+// the row into NaN through 0 * inf.  NaN stays NaN.
+__device__ __forceinline__ _Float16 v_to_f16(float x) {
+  return (_Float16)(fabsf(x) > 65504.0f ? __builtin_copysignf(65504.0f, x) : x);
+}
 
 // Key stored at position p of a 32-key group of a staged V^T tile.  Position
 // 8*g + 4*h + j holds key 16*h + 4*g + j: lane group g of a 16x16 score block
@@ -308,6 +321,10 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     acc_r[fb] = f32x4{};
   }
   float m_run = kMinit;
+  // The row's R enters the fp16 products as R * 2^-r_exp (r_exp = 0 until some
+  // |R| of the row exceeds kRMax); acc_r and c carry the same factor, removed in
+  // the epilogue.  The four lanes of a query hold the same value.
+  float r_exp = 0.f;
   // l = sum_j P_ij and c = sum_j T_ij, accumulated on the matrix cores: the
   // product of an all-ones 16x32 block with P^T (or T^T) holds the per-query
   // sums in every row, so each lane's four values are copies of its query's.
@@ -435,16 +452,48 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 
   f32x4 sc[4], rc[4];     // scores of the tile being finished
 
+  // Rare path of the R range check: some row of the wave has |R| > kRMax in the
+  // tile whose R is `ra`.  Each such row takes the smallest power of two that
+  // brings its largest |R| to at most kRMax and applies it, exactly, to what
+  // the fp16 products of its later tiles see (its rho fragments), to this
+  // tile's R and to the r-weighted sums gathered so far (acc_r, acc_c).
+  auto rescale_r = [&](f32x4 (&ra)[4], float rm) {
+    // keeps this path behind its branch: without the barrier the compiler
+    // speculates it into every tile with a factor of one
+    asm volatile("" ::: "memory");
+    float rr = lane_xor16(rm, Max{});
+    rr = lane_xor32(rr, Max{});
+    // rr in [2^e, 2^(e+1)) with e >= 11: scaling by 2^-(e-10) lands in [2^10, 2^11)
+    const int de = rr > kRMax ? __builtin_amdgcn_frexp_expf(rr) - 11 : 0;
+    const float f = __builtin_ldexpf(1.0f, -de);
+    r_exp += (float)de;
+    acc_c *= f;
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb) acc_r[fb] *= f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) ra[kb] *= f;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rf[kk][e] = (__bf16)((float)rf[kk][e] * f);
+    }
+  };
   // Causal mask (the wave's last tile is its only diagonal tile) and the scaled
   // row max of one tile's scores; the four lanes that share a query combine.
-  auto tile_max = [&](f32x4 (&sa)[4], int kt_, auto diag_c) -> float {
+  // With the correction, masked keys also get R = 0 (they never reach a row's
+  // sums, so their |R| must not steer its scale), and the tile's |R| is checked
+  // against kRMax before its fp16 conversion.
+  auto tile_max = [&](f32x4 (&sa)[4], f32x4 (&ra)[4], int kt_, auto diag_c) -> float {
     if constexpr (decltype(diag_c)::value) {
       const int lim = pos0 + qi - kt_ * PF_BC - 4 * g4;   // key offset 16*kb + j kept iff <= lim
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (16 * kb + j > lim) sa[kb][j] = -INFINITY;
+          if (16 * kb + j > lim) {
+            sa[kb][j] = -INFINITY;
+            if constexpr (CORR) ra[kb][j] = 0.f;
+          }
         }
       }
     }
@@ -453,6 +502,15 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sa[kb][j]);
+    }
+    if constexpr (CORR) {
+      float rm = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rm = fmaxf(rm, fabsf(ra[kb][j]));
+      }
+      if (__any(rm > kRMax)) rescale_r(ra, rm);
     }
     mx = lane_xor16(mx, Max{});
     mx = lane_xor32(mx, Max{});
@@ -533,7 +591,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
       for (int e = 0; e < KP; ++e) {
         const uint32_t w = in[e][j >> 1];
-        o[e] = (_Float16)__uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
+        o[e] = v_to_f16(__uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16)));
       }
       *reinterpret_cast<f16xkp*>(vtl + LY::v_off(8 * fc + j, c) + e0) = o;
     }
@@ -554,15 +612,15 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     load_k(min(kt_ + 2, t_end - 1), P, KHalf{}, KAll1{});
     load_v(min(kt_ + 1, t_end - 1), 1 - P);
     softmax_pv(par, cs, cr);
-    return tile_max(ns, kt_ + 1, diag_next);
+    return tile_max(ns, nr, kt_ + 1, diag_next);
   };
 
   f32x4 sn[4], rn[4];     // the other score register set of the pipelined loop
   if constexpr (PIPE) {
     if (w_end > t_beg) {
       scores(std::integral_constant<int, 0>{}, sc, rc);
-      m_run = needs_mask(t_beg) ? tile_max(sc, t_beg, std::true_type{})
-                                : tile_max(sc, t_beg, std::false_type{});
+      m_run = needs_mask(t_beg) ? tile_max(sc, rc, t_beg, std::true_type{})
+                                : tile_max(sc, rc, t_beg, std::false_type{});
     }
     // iteration 0 overwrites K buffer 0: every wave must be done reading it
     __syncthreads();
@@ -594,8 +652,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         }
       } else if constexpr (FUSEV == 0) {
         scores(par, cs, cr);
-        const float m_tile = needs_mask(kt) ? tile_max(cs, kt, std::true_type{})
-                                            : tile_max(cs, kt, std::false_type{});
+        const float m_tile = needs_mask(kt) ? tile_max(cs, cr, kt, std::true_type{})
+                                            : tile_max(cs, cr, kt, std::false_type{});
         if (kt == t_beg) m_run = m_tile;        // accumulators are still zero
         rescale_to(m_tile);
         softmax_pv(par, cs, cr);
@@ -608,8 +666,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       if (wave_u < FUSEV) {
         if (kt < w_end) {
           scores(par, cs, cr);
-          const float m_tile = needs_mask(kt) ? tile_max(cs, kt, std::true_type{})
-                                              : tile_max(cs, kt, std::false_type{});
+          const float m_tile = needs_mask(kt) ? tile_max(cs, cr, kt, std::true_type{})
+                                              : tile_max(cs, cr, kt, std::false_type{});
           if (kt == t_beg) m_run = m_tile;      // accumulators are still zero
           rescale_to(m_tile);
         }
@@ -633,11 +691,13 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   }
 
   // epilogue: o = o_sa - g (u - o_sa * rbar), o_sa = O/l, u = A_r/l, rbar = c/l
+  // (A_r and c times 2^r_exp: the row's R scale comes off here)
   const float l_tot = acc_l[0];
   const float c_tot = acc_c[0];
   if constexpr (SPLIT) {
-    // the split's unnormalised state, relative to 2^m_run; a row whose keys all
-    // precede this split leaves a record no combine reads
+    // the split's unnormalised state, relative to 2^m_run, with c and sum p r v
+    // relative to 2^-r_exp; a row whose keys all precede this split leaves a
+    // record no combine reads
     if (qi < n_q) {
       constexpr int RF = 2 * D + 4;
       float* rec = ca.part + (((size_t)(c0 + qi) * H + h) * ca.n_split + sp) * RF;
@@ -646,13 +706,14 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         *reinterpret_cast<f32x4*>(rec + 4 + 16 * fb + 4 * g4) = acc_o[fb];
         *reinterpret_cast<f32x4*>(rec + 4 + D + 16 * fb + 4 * g4) = acc_r[fb];
       }
-      if (g4 == 0) *reinterpret_cast<f32x4*>(rec) = f32x4{m_run, l_tot, c_tot, 0.f};
+      if (g4 == 0) *reinterpret_cast<f32x4*>(rec) = f32x4{m_run, l_tot, c_tot, r_exp};
     }
     return;
   }
   if (qi < n_q) {
     const float inv = 1.0f / l_tot;
-    const float rbar = c_tot * inv;
+    const float inv_r = CORR ? __builtin_ldexpf(inv, (int)r_exp) : inv;
+    const float rbar = c_tot * inv_r;
     const float gh = CORR ? gate[h] : 0.f;
     float* orow = out + qbase + (size_t)qi * qstride;
 #pragma unroll
@@ -662,7 +723,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       for (int j = 0; j < 4; ++j) {
         const float osa = acc_o[fb][j] * inv;
         if constexpr (CORR) {
-          const float uu = acc_r[fb][j] * inv;
+          const float uu = acc_r[fb][j] * inv_r;
           o[j] = osa - gh * (uu - osa * rbar);
         } else {
           o[j] = osa;
@@ -674,7 +735,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float osa = acc_o[fb][j] * inv;
-          cv[j] = acc_r[fb][j] * inv - osa * rbar;
+          cv[j] = acc_r[fb][j] * inv_r - osa * rbar;
         }
         *reinterpret_cast<f32x4*>(corr_out + head + (size_t)qi * D + 16 * fb + 4 * g4) = cv;
       }
@@ -747,7 +808,8 @@ void stage_v_kernel(const __bf16* __restrict__ v, TOUT* __restrict__ vt, int L, 
     for (int e = 0; e < 8; ++e) {
       const int key = vt_key_of_pos(key0 + e);
       const float x = __uint_as_float((uint32_t)tile[key * PITCH + f] << 16);
-      o[e] = (TOUT)x;
+      if constexpr (std::is_same<TOUT, _Float16>::value) o[e] = v_to_f16(x);
+      else o[e] = (TOUT)x;
     }
     *reinterpret_cast<outx8*>(dst + (size_t)ch * 8) = o;
   }
@@ -870,10 +932,12 @@ void chunk_combine_kernel(const float* __restrict__ gate, float* __restrict__ ou
   for (int sp = 0; sp < ns; ++sp) {
     const float* r = rec + (size_t)sp * RF;
     const float w = __builtin_amdgcn_exp2f(r[0] - M);
+    // c and sum p r v of a split are relative to 2^-r_exp (record slot 3)
+    const float wr = __builtin_ldexpf(w, (int)r[3]);
     l += w * r[1];
-    c += w * r[2];
+    c += wr * r[2];
     a += w * r[4 + f];
-    bv += w * r[4 + D + f];
+    bv += wr * r[4 + D + f];
   }
   const float inv = 1.0f / l;
   const float osa = a * inv;

@@ -306,3 +306,58 @@ def test_chunk_random_short_chunks(seed):
     print(f"short {seed}: B{B} H{H} ctx{ctx} n{n} split {split}: max-abs {err:.3e}", flush=True)
     assert err <= TOL
     assert torch.equal(staged, out)
+
+
+def _chunk_row_bounds(inp):
+    """Per-row rounding bound for large rho (see the prefill test of the same
+    name): 2e-2 plus 4 * 2^-11 * g * (sum_j w_j |r_j| |v_j| + sum_j w_j |r_j| sum_j w_j |v_j|)
+    over the row's causal cache prefix."""
+    h = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in inp.items()}
+    q, rho = h["q"].double().numpy(), h["rho"].double().numpy()
+    kc, vc = h["kcache"].double().numpy(), h["vcache"].double().numpy()
+    gate = h["gate"].double().numpy()
+    cu, ctx = h["cu_q"].tolist(), h["ctx"].tolist()
+    T, H, d = q.shape
+    bnd = np.full((T, H, d), np.nan)
+    for b in range(len(ctx)):
+        for j, t in enumerate(range(cu[b], cu[b + 1])):
+            p = ctx[b] + j
+            for hh in range(H):
+                K, V = kc[b, hh, : p + 1], vc[b, hh, : p + 1]
+                s = (K @ q[t, hh]) / np.sqrt(d)
+                w = np.exp(s - s.max())
+                w /= w.sum()
+                r = np.abs(K @ rho[t, hh])
+                a = (w * r) @ np.abs(V) + (w @ r) * (w @ np.abs(V))
+                bnd[t, hh] = TOL + 4 * 2.0 ** -11 * gate[hh] * a
+    return bnd
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n", [[40, 130], [40, 20]], ids=["long", "short"])
+@pytest.mark.parametrize("split", [0, 128, 4096])
+def test_chunk_large_rho(d, n, split):
+    """|<rho,k>| up to about 1e5: the chunk kernels scale such rows by a power of
+    two, split records carry the scale (slot 3) and the combine removes it.  Per
+    call and with the staged V cache (bit-identical), split and not split;
+    [40, 20] at d = 128 runs the in-kernel V conversion."""
+    plx = _plx()
+    ctx = [500, 37]
+    inp = wl.chunk_inputs(2, d, ctx, n, seed=1400 + d + sum(n), device="cuda", rho_std=1.0)
+    inp["rho"] = (inp["rho"].float() * (2.2e4 / d ** 0.5)).to(torch.bfloat16)
+    out = _run(inp, split_keys=split)
+    vt = plx.prefill_stage_v(inp["vcache"])
+    out_vt = plx.prefill_chunk(inp["q"], inp["kcache"], None, inp["rho"], inp["gate"],
+                               inp["cu_q"], inp["ctx"], inp["max_q"], vt_cache=vt,
+                               split_keys=split)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_vt)
+    got = out.cpu().double().numpy()
+    assert np.isfinite(got).all()
+    ref = _oracle(inp)
+    bnd = _chunk_row_bounds(inp)
+    err = np.abs(got - ref)
+    print(f"chunk large rho d{d} n{n} split {split}: max-abs {err.max():.3e}, "
+          f"max |ref| {np.abs(ref).max():.3e}, max error/bound {(err / bnd).max():.3f}",
+          flush=True)
+    assert np.all(err <= bnd)

@@ -183,6 +183,108 @@ def test_workload2_every_head():
     assert worst <= TOL["bf16"]
 
 
+_W5 = {}
+
+
+def _workload5():
+    """Workload 5 (B2 H32 L16384 d64, duplicated key runs), its GPU output in the
+    benchmark's launch configuration and fp64 host copies, made once per session."""
+    if not _W5:
+        inp = wl.make_workload(5, device="cuda")
+        out = _plx().prefill(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"])
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+        _W5["out"] = _host(out).double().numpy()
+        _W5["h"] = {k: _host(inp[k]).double().numpy() for k in ("q", "k", "v", "rho", "gate")}
+        del inp, out
+        torch.cuda.empty_cache()
+    return _W5
+
+
+@pytest.mark.parametrize("part", range(8))
+def test_workload5_every_head(part):
+    """Workload 5 compared with the expanded-form oracle on every output element
+    of all 64 heads, eight heads per test (about 3 s of oracle time per head)."""
+    w = wl.WORKLOADS[5]
+    st = _workload5()
+    h, got = st["h"], st["out"]
+    worst = 0.0
+    for idx in range(8 * part, 8 * part + 8):
+        b, hh = divmod(idx, w.H)
+        ref = po.prefill_head(h["q"][b, hh], h["k"][b, hh], h["v"][b, hh], h["rho"][b, hh],
+                              float(h["gate"][hh]), w.scale)
+        err = _maxerr(got[b, hh], ref)
+        worst = max(worst, err)
+        print(f"workload 5 head ({b},{hh}): max-abs {err:.3e}", flush=True)
+    assert worst <= TOL["bf16"]
+
+
+def _row_bound(q, k, v, rho, g, scale, base):
+    """Rounding bound of each prefill row of one head when rho is large: the
+    fp16 roundings of P, R (after the row's power-of-two scale) and T = P*R
+    each carry a relative error of at most 2^-11 (four roundings with the
+    weight normalisation), so the correction sum_j w_j r_j v_j - o_sa sum_j w_j r_j
+    moves by at most 4 * 2^-11 * g * (sum_j w_j |r_j| |v_j| + sum_j w_j |r_j|
+    sum_j w_j |v_j|), plus the bf16-path bound for the rest."""
+    L = q.shape[0]
+    S = scale * (q @ k.T)
+    S = np.where(np.tril(np.ones((L, L), bool)), S, -np.inf)
+    W = np.exp(S - S.max(1, keepdims=True))
+    W /= W.sum(1, keepdims=True)
+    R = np.abs(rho @ k.T)
+    a = (W * R) @ np.abs(v) + (W * R).sum(1, keepdims=True) * (W @ np.abs(v))
+    return base + 4 * 2.0 ** -11 * g * a
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_large_rho_is_rescaled_exactly(d):
+    """|<rho,k>| up to about 1e5 (far past what fp16 T = P*R holds unscaled):
+    the kernel scales each such row by a power of two and unscales it in fp32.
+    Every row must be finite and within its rounding bound of the oracle."""
+    B, H, L = 1, 3, 300
+    inp = wl.prefill_inputs(B, H, L, d, "bf16", seed=760 + d, device="cuda", rho_std=1.0,
+                            gate=("uniform", 0.2, 1.0))
+    # heads 0, 1, 2: |r| up to about 1e5, 4e3 and 1e2
+    for hh, std in enumerate((2.2e4 / d ** 0.5, 900.0 / d ** 0.5, 22.0 / d ** 0.5)):
+        inp["rho"][:, hh] = (inp["rho"][:, hh].float() * std).to(torch.bfloat16)
+    out = _run(inp)
+    assert np.isfinite(out).all()
+    h = {k: _host(x).double().numpy() for k, x in inp.items()}
+    rmax = np.abs(np.einsum("bhid,bhjd->bhij", h["rho"], h["k"])).max(axis=(0, 2, 3))
+    print(f"d{d}: max |<rho,k>| per head {rmax}", flush=True)
+    assert rmax[0] > 5e4
+    ref = po.prefill(h["q"], h["k"], h["v"], h["rho"], h["gate"])
+    for hh in range(H):
+        bnd = _row_bound(h["q"][0, hh], h["k"][0, hh], h["v"][0, hh], h["rho"][0, hh],
+                         float(h["gate"][hh]), 1.0 / np.sqrt(d), TOL["bf16"])
+        err = np.abs(out[0, hh] - ref[0, hh])
+        rel = float((err / bnd).max())
+        print(f"d{d} head {hh}: max-abs {err.max():.3e}, max |ref| {np.abs(ref[0, hh]).max():.3e},"
+              f" max error/bound {rel:.3f}", flush=True)
+        assert np.all(err <= bnd)
+    # row 0 still reproduces v_0 exactly (one key: no correction at any scale)
+    assert np.array_equal(out[:, :, 0], h["v"][:, :, 0])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_value_beyond_fp16_range_stays_in_its_rows(d):
+    """A value past fp16's range at key j (clamped to +-65504 in the fp16 copy)
+    must not change any row that does not attend it: rows i < j, including those
+    in j's own 64-key tile where j is a masked key, stay bit-identical and
+    finite."""
+    B, H, L = 1, 2, 200
+    inp = wl.prefill_inputs(B, H, L, d, "bf16", seed=780 + d, device="cuda", rho_std=0.5,
+                            gate=("uniform", 0.2, 1.0))
+    base = _run(inp)
+    j = 150                                   # inside the tile of keys 128..191
+    inp["v"][0, 1, j, 3] = 1.0e6
+    inp["v"][0, 1, j, 4] = -float("inf")
+    out = _run(inp)
+    assert np.array_equal(out[0, 1, :j], base[0, 1, :j])
+    assert np.array_equal(out[0, 0], base[0, 0])
+    assert np.isfinite(out[0, 1, :j]).all()
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_long_sequence_sampled(d):
     """A single long head (L = 65537, one past a power of two): sampled rows,
