@@ -17,7 +17,9 @@
 //   accumulators sum p v and sum p r v for its features.  At the end the
 //   groups of all four waves merge through LDS into one partial record.
 // decode_combine_kernel: one workgroup per (b,h) merges the records of its
-//   splits, rescaling by 2^(m_s - M), and applies the output formula.
+//   splits, rescaling by 2^(m_s - M), with the splits spread over the lanes of
+//   the workgroup (butterfly reductions across lanes, then across waves), and
+//   applies the output formula.
 //
 // CORR = false compiles the covariance branch out of both kernels (no rho
 // reads, no <rho,k>, c or sum p r v; records of d+4 floats): plain softmax
@@ -207,45 +209,117 @@ void decode_split_kernel(const T* __restrict__ q, const T* __restrict__ kc,
   }
 }
 
+// Merge of (m, l, c) triples in the base-2 log domain: both sides rescaled to
+// the larger running max.
+struct Mlc {
+  float m, l, c;
+};
+__device__ __forceinline__ Mlc mlc_merge(Mlc a, Mlc b) {
+  const float M = fmaxf(a.m, b.m);
+  const float wa = __builtin_amdgcn_exp2f(a.m - M), wb = __builtin_amdgcn_exp2f(b.m - M);
+  return Mlc{M, a.l * wa + b.l * wb, a.c * wa + b.c * wb};
+}
+__device__ __forceinline__ Mlc mlc_xor(Mlc x, int mask) {
+  return Mlc{__shfl_xor(x.m, mask), __shfl_xor(x.l, mask), __shfl_xor(x.c, mask)};
+}
+
 // Merge the split records of one (b,h) and write o = o_sa - g (u - o_sa rbar)
-// (o = o_sa without the correction).
+// (o = o_sa without the correction).  One workgroup of 256 threads per stream,
+// splits spread over lanes:
+//   1. every thread folds the (m, l, c) of splits tid, tid+256, ... into one
+//      triple, and the triples of the workgroup meet in a butterfly across the
+//      64 lanes of each wave and then across the 4 waves (LDS): the stream's
+//      max M, l and c;
+//   2. the 2D (D without the correction) feature sums are split into float4
+//      columns; NSG groups of threads take every NSG-th split, so each thread
+//      issues all its 16-byte record loads at once (unrolled) and accumulates
+//      2^(m_s - M) times them;
+//   3. the groups' column sums meet in LDS, in a fixed order.
+// The merge order is fixed, so results are deterministic.
 template <int D, bool CORR>
-__global__ __launch_bounds__(D)
+__global__ __launch_bounds__(256)
 void decode_combine_kernel(const float* __restrict__ part, const float* __restrict__ gate,
                            const int* __restrict__ seqlens, float* __restrict__ out,
                            int H, int Lmax, int C, int S) {
+  constexpr int RF = rec_floats<D, CORR>();
+  constexpr int NF = RF - 4;                 // feature floats per record
+  // float4 columns of the correction's record layout, used by both variants so
+  // that the softmax-only twin sums sum p v in the same order (its columns past
+  // NF / 4 stay idle): a zero probe then gives bit-identical outputs
+  constexpr int NC = (2 * D) / 4;
+  constexpr int NSG = 256 / NC;              // split groups
+  static_assert(NC * NSG == 256, "columns x groups must cover the workgroup");
+  __shared__ Mlc s_w[4];
+  __shared__ f32x4 s_acc[NSG][NC];
+
   const int bh = blockIdx.x;
   const int b = bh / H, h = bh % H;
-  const int f = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int Lb = min(max(seqlens[b], 0), Lmax);
   const int ns = (Lb + C - 1) / C;
   float* o = out + (size_t)bh * D;
-  if (ns == 0) {
-    o[f] = 0.f;
+  if (ns == 0) {                              // uniform over the workgroup
+    if (tid < D) o[tid] = 0.f;
     return;
   }
-  constexpr int RF = rec_floats<D, CORR>();
   const float* rec = part + (size_t)bh * S * RF;
-  float M = kMinit;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, rec[(size_t)s * RF]);
-  float l = 0.f, c = 0.f, a = 0.f, bv = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float* r = rec + (size_t)s * RF;
-    const float w = __builtin_amdgcn_exp2f(r[0] - M);
-    l += w * r[1];
-    a += w * r[4 + f];
-    if constexpr (CORR) {
-      c += w * r[2];
-      bv += w * r[4 + D + f];
-    }
+
+  // 1. (M, l, c) of the stream
+  Mlc t{kMinit, 0.f, 0.f};
+  for (int sp = tid; sp < ns; sp += 256) {
+    const f32x4 hd = *reinterpret_cast<const f32x4*>(rec + (size_t)sp * RF);
+    t = mlc_merge(t, Mlc{hd[0], hd[1], CORR ? hd[2] : 0.f});
   }
-  const float inv = 1.0f / l;
-  const float osa = a * inv;
-  if constexpr (CORR) {
-    const float uu = bv * inv;
-    o[f] = osa - gate[h] * (uu - osa * (c * inv));
-  } else {
-    o[f] = osa;
+#pragma unroll
+  for (int mask = 1; mask < 64; mask <<= 1) t = mlc_merge(t, mlc_xor(t, mask));
+  if (lane == 0) s_w[wave] = t;
+  __syncthreads();
+  const Mlc tot = mlc_merge(mlc_merge(s_w[0], s_w[1]), mlc_merge(s_w[2], s_w[3]));
+  const float M = tot.m;
+
+  // 2. weighted feature sums: thread (group sg, column cc)
+  const int cc = tid % NC, sg = tid / NC;
+  f32x4 acc = {};
+  constexpr int UNR = 8;
+  for (int s0 = sg; cc < NF / 4 && s0 < ns; s0 += UNR * NSG) {
+    f32x4 v[UNR];
+    float w[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int sp = s0 + u * NSG;
+      if (sp < ns) {
+        const float* r = rec + (size_t)sp * RF;
+        w[u] = r[0];
+        v[u] = *reinterpret_cast<const f32x4*>(r + 4 + 4 * cc);
+      } else {
+        w[u] = -INFINITY;
+        v[u] = f32x4{};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) acc += __builtin_amdgcn_exp2f(w[u] - M) * v[u];
+  }
+  s_acc[sg][cc] = acc;
+  __syncthreads();
+
+  // 3. column sums over the groups, then the output formula
+  if (tid < D) {
+    const int f = tid;
+    float a = 0.f, bv = 0.f;
+#pragma unroll
+    for (int g = 0; g < NSG; ++g) {
+      a += s_acc[g][f >> 2][f & 3];
+      if constexpr (CORR) bv += s_acc[g][(D + f) >> 2][(D + f) & 3];
+    }
+    const float inv = 1.0f / tot.l;
+    const float osa = a * inv;
+    if constexpr (CORR) {
+      const float uu = bv * inv;
+      o[f] = osa - gate[h] * (uu - osa * (tot.c * inv));
+    } else {
+      o[f] = osa;
+    }
   }
 }
 
@@ -285,7 +359,7 @@ hipError_t launch_decode_split(const void* q, const void* kc, const void* vc, co
 template <int D, bool CORR>
 static void launch_combine_t(const float* part, const float* gate, const int* seqlens,
                              float* out, int B, int H, int Lmax, int C, int S, hipStream_t s) {
-  hipLaunchKernelGGL((decode_combine_kernel<D, CORR>), dim3((unsigned)(B * H)), dim3(D), 0, s,
+  hipLaunchKernelGGL((decode_combine_kernel<D, CORR>), dim3((unsigned)(B * H)), dim3(256), 0, s,
                      part, gate, seqlens, out, H, Lmax, C, S);
 }
 
