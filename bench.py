@@ -1,18 +1,26 @@
 """Benchmark of the Parallax forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+                    [--no-softmax] [--no-backward] [--no-chunk] [--no-sweep]
 
 One step is one pass of the whole hot path over resident synthetic inputs:
   1. bf16 causal prefill, B=4 H=16 L=4096 d=128 (V staging + fused kernel);
   2. bf16 decode, B=64 H=16 d=128, 8192 cached keys per sequence
      (split-KV partials + combine).
 Every launch is bracketed by HIP events on the stream it runs on (torch's
-current stream, which the library is handed).  `value` is the prefill
-throughput in TFLOP/s (algorithmic flops 8*d*B*H*L(L+1)/2 over the time of both
-prefill kernels); the decode throughput in GB/s (algorithmic bytes: K and V
-over the valid lengths plus q, rho, out, gate, seqlens) is reported beside it.
-`roofline` describes the dominant kernel (the fused prefill kernel), and the
-decode block carries its own for the split-KV kernel.
+current stream, which the library is handed).  Per kernel the line reports the
+median, mean, min and max over the timed steps and the spread (max - min) /
+median.  `value` is the prefill throughput in TFLOP/s: algorithmic flops
+8*d*B*H*L(L+1)/2 over the median per-step time of both prefill kernels.  The
+decode throughput in GB/s (algorithmic bytes: K and V over the valid lengths
+plus q, rho, out, gate, seqlens) is reported beside it.
+
+`roofline` describes the kernel that `value` measures, the fused prefill
+kernel, against the bf16 MFMA peak.  The step's longest kernel is the decode
+split pass (HBM-bound); its roofline is `decode.roofline`.  `rooflines` lists
+every timed hot-path kernel on every full-size workload, each with the HBM
+bytes its rocprofv3 counters read (`traffic`, null when no counter
+measurement matches the current kernel source).
 
 Unless --no-extra is given, the two other full-size workloads (long ragged
 decode and the d=64 prefill) are timed too and reported under "extra".
@@ -28,8 +36,11 @@ serving loop that keeps the staged V cache and re-stages only the appended
 rows' tiles.
 "softmax_relative" times the same kernels with the correction branch compiled
 out (plain causal softmax attention) against the Parallax kernels on each
-workload, alternating the two launch by launch, and reports the time ratio.
+workload, alternating the two launch by launch, and reports the time ratio;
+"softmax_sweep" does the same over batch sizes and context lengths (prefill
+L 1k-64k at d 64 and 128, decode B 1-64 x L 8k-128k).
 The CPU baseline times the fp64 oracle on a bounded sample on the host.
+"checksums" holds the fp64 sum of every input tensor of the step.
 Prints exactly one JSON line on stdout.
 """
 from __future__ import annotations
@@ -38,6 +49,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -51,8 +63,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {   # the files whose text determines each kernel's code
     "prefill_bf16_kernel": ["parallax_local_linear_amd/csrc/prefill_bf16.hip",
                             "parallax_local_linear_amd/csrc/plx_common.h"],
+    "stage_v_kernel": ["parallax_local_linear_amd/csrc/prefill_bf16.hip",
+                       "parallax_local_linear_amd/csrc/plx_common.h"],
     "decode_split_kernel": ["parallax_local_linear_amd/csrc/decode.hip",
                             "parallax_local_linear_amd/csrc/plx_common.h"],
+    "decode_combine_kernel": ["parallax_local_linear_amd/csrc/decode.hip",
+                              "parallax_local_linear_amd/csrc/plx_common.h"],
 }
 
 
@@ -68,17 +84,37 @@ def src_sha(kernel):
     return h.hexdigest()[:16]
 
 
-def traffic(kernel):
-    """HBM bytes per launch measured with rocprofv3 counters for this exact
-    kernel source, or None when no measurement matches the current source."""
+def traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` measured with rocprofv3
+    counters for this exact kernel source, or None when no measurement matches
+    the current source."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f).get(kernel)
+            t = json.load(f).get(f"{kernel}@{workload}")
     except (OSError, ValueError):
         return None
     if not t or t.get("src_sha") != src_sha(kernel):
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def roofline(kernel, template, workload, bound, work, ms):
+    """Roofline object of one kernel: algorithmic work per launch over its
+    median launch time, against the MI355X peak of its bound."""
+    if bound == "mfma":
+        achieved, peak, unit = work / (ms * 1e-3) / 1e12, PEAK_MFMA_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = work / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    return {"kernel": template, "workload": workload, "bound": bound,
+            "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "ms": round(ms, 4),
+            "traffic": traffic(kernel, workload)}
+
+
+def _median(xs):
+    s = sorted(xs)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
 
 
 class Timer:
@@ -96,73 +132,122 @@ class Timer:
         b.record()
         self.ev.setdefault(label, []).append((a, b))
 
+    def times(self, label, skip=0):
+        return [a.elapsed_time(b) for a, b in self.ev[label][skip:]]
+
     def ms(self, label, skip=0):
-        pairs = self.ev[label][skip:]
-        return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+        """Median launch time in ms."""
+        return _median(self.times(label, skip))
+
+    def stats(self, label, skip=0):
+        return stats(self.times(label, skip))
 
     def reset(self):
         self.ev = {}
 
 
-def cpu_threads():
+def stats(xs):
+    med = _median(xs)
+    return {"median": round(med, 4), "mean": round(sum(xs) / len(xs), 4),
+            "min": round(min(xs), 4), "max": round(max(xs), 4),
+            "spread": round((max(xs) - min(xs)) / med, 4) if med > 0 else None, "n": len(xs)}
+
+
+def checksums(inp):
+    """fp64 sum of every tensor input (computed on the device, outside timing)."""
+    return {k: float(v.double().sum()) for k, v in inp.items() if hasattr(v, "double")}
+
+
+def cpu_info():
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = None, os.cpu_count()
     try:
         from threadpoolctl import threadpool_info
-        n = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
-        if n:
-            return max(n)
+        for p in threadpool_info():
+            if p.get("user_api") == "blas":
+                blas = f"{p.get('internal_api')} {p.get('version')} ({p.get('architecture')})"
+                threads = p.get("num_threads", threads)
+                break
     except Exception:
         pass
-    return os.cpu_count()
+    import numpy as np
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "blas": blas,
+            "numpy": np.__version__}, threads
 
 
 def cpu_baseline_prefill(inp, w, budget_s=12.0):
     """fp64 oracle (expanded form) on whole heads of the prefill workload until
-    the time budget is spent; TFLOP/s over the same algorithmic count."""
+    the time budget is spent; TFLOP/s over the same algorithmic count.  The
+    device-to-host copy and the bf16 -> fp64 conversion are timed separately."""
     from oracle import parallax_oracle as po
     import workloads as wl
     heads = 0
-    t_tot = 0.0
+    t_tot = t_d2h = t_conv = 0.0
+    info, threads = cpu_info()
     for idx in range(w.B * w.H):
         b, h = divmod(idx, w.H)
-        arrs = {k: inp[k][b, h].float().cpu().double().numpy() for k in ("q", "k", "v", "rho")}
-        g = float(inp["gate"][h])
         t0 = time.perf_counter()
+        host = {k: inp[k][b, h].cpu() for k in ("q", "k", "v", "rho")}
+        t1 = time.perf_counter()
+        arrs = {k: x.float().double().numpy() for k, x in host.items()}
+        t2 = time.perf_counter()
+        g = float(inp["gate"][h])
+        t3 = time.perf_counter()
         po.prefill_head(arrs["q"], arrs["k"], arrs["v"], arrs["rho"], g, w.scale)
-        t_tot += time.perf_counter() - t0
+        t_tot += time.perf_counter() - t3
+        t_d2h += t1 - t0
+        t_conv += t2 - t1
         heads += 1
         if t_tot >= budget_s:
             break
     flops = wl.prefill_flops(1, heads, w.L, w.d)
-    return {"value": flops / t_tot / 1e12, "unit": "TFLOP/s", "cores": cpu_threads(),
+    return {"value": flops / t_tot / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{heads} of {w.B * w.H} heads of the B{w.B} H{w.H} L{w.L} d{w.d} "
-                      f"prefill, fp64 expanded form, {t_tot:.1f}s"}
+                      f"prefill, fp64 expanded form, {t_tot:.1f}s",
+            "oracle_s": round(t_tot, 3), "d2h_s": round(t_d2h, 3),
+            "bf16_to_fp64_s": round(t_conv, 3), **info}
 
 
 def cpu_baseline_decode(inp, w, budget_s=6.0):
     """fp64 oracle on whole decode streams until the time budget is spent."""
     from oracle import parallax_oracle as po
     H, d = w.H, w.d
-    n_streams, nbytes, t_tot = 0, 0, 0.0
+    n_streams, nbytes = 0, 0
+    t_tot = t_d2h = t_conv = 0.0
+    info, threads = cpu_info()
     sl = inp["seqlens"].cpu().tolist()
     for idx in range(w.B * H):
         b, h = divmod(idx, H)
         n = sl[b]
-        K = inp["kcache"][b, h, :n].float().cpu().double().numpy()
-        V = inp["vcache"][b, h, :n].float().cpu().double().numpy()
-        q = inp["q"][b, h].float().cpu().double().numpy()
-        r = inp["rho"][b, h].float().cpu().double().numpy()
         t0 = time.perf_counter()
-        po.decode_stream(q, K, V, r, float(inp["gate"][h]), w.scale)
-        t_tot += time.perf_counter() - t0
+        host = {"K": inp["kcache"][b, h, :n].cpu(), "V": inp["vcache"][b, h, :n].cpu(),
+                "q": inp["q"][b, h].cpu(), "r": inp["rho"][b, h].cpu()}
+        t1 = time.perf_counter()
+        a = {k: x.float().double().numpy() for k, x in host.items()}
+        t2 = time.perf_counter()
+        po.decode_stream(a["q"], a["K"], a["V"], a["r"], float(inp["gate"][h]), w.scale)
+        t_tot += time.perf_counter() - t2
+        t_d2h += t1 - t0
+        t_conv += t2 - t1
         n_streams += 1
         nbytes += n * 2 * d * 2 + 2 * d * 2 + d * 4
         if t_tot >= budget_s:
             break
-    return {"value": nbytes / t_tot / 1e9, "unit": "GB/s", "cores": cpu_threads(),
+    return {"value": nbytes / t_tot / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n_streams} of {w.B * H} streams of the decode workload, fp64, "
-                      f"bytes counted as bf16, {t_tot:.1f}s"}
+                      f"bytes counted as bf16, {t_tot:.1f}s",
+            "oracle_s": round(t_tot, 3), "d2h_s": round(t_d2h, 3),
+            "bf16_to_fp64_s": round(t_conv, 3), **info}
 
 
 def main():
@@ -177,6 +262,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the training forward and backward timing")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunked prefill timing")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the softmax-relative sweep over batch sizes and lengths")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size kernel for scaling HBM byte counters)")
@@ -196,6 +283,7 @@ def main():
     log("generating inputs")
     pin = wl.make_workload(2, device=dev)
     din = wl.make_workload(3, device=dev)
+    sums = {wp.name: checksums(pin), wd.name: checksums(din)}
     B, H, L, d = wp.B, wp.H, wp.L, wp.d
     vt = torch.empty(plx.prefill_workspace_bytes(B, H, L, d), dtype=torch.uint8, device=dev)
     pout = torch.empty((B, H, L, d), dtype=torch.float32, device=dev)
@@ -229,17 +317,32 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    ms = {k: tm.ms(k) for k in ("stage_v", "attend", "partials", "combine")}
+    st = {k: tm.stats(k) for k in ("stage_v", "attend", "partials", "combine")}
+    ms = {k: v["median"] for k, v in st.items()}
+    pre_steps = [a + b for a, b in zip(tm.times("stage_v"), tm.times("attend"))]
+    dec_steps = [a + b for a, b in zip(tm.times("partials"), tm.times("combine"))]
     ms_step = wall * 1e3 / args.steps
     flops = wl.prefill_flops(B, H, L, d)
-    pre_ms = ms["stage_v"] + ms["attend"]
+    pre_ms = _median(pre_steps)
     value = flops / (pre_ms * 1e-3) / 1e12
-    att_tf = flops / (ms["attend"] * 1e-3) / 1e12
-    t_att = traffic("prefill_bf16_kernel")
     dbytes = wl.decode_bytes(din["seqlens"].tolist(), wd.H, wd.d)
-    dec_ms = ms["partials"] + ms["combine"]
-    part_gbs = dbytes / (ms["partials"] * 1e-3) / 1e9
-    t_dec = traffic("decode_split_kernel")
+    dec_ms = _median(dec_steps)
+    rl_att = roofline("prefill_bf16_kernel", "prefill_bf16_kernel<128>", wp.name, "mfma", flops,
+                      ms["attend"])
+    rl_dec = roofline("decode_split_kernel", "decode_split_kernel<bf16,128>", wd.name, "hbm",
+                      dbytes, ms["partials"])
+    # staging moves V once in and its fp16 copy once out; the combine reads the
+    # split records and writes the output
+    vt_bytes = 2 * B * H * L * d * 2
+    comb_bytes = wd.B * wd.H * S * (2 * wd.d + 4) * 4 + wd.B * wd.H * wd.d * 4
+    rooflines = [
+        rl_att,
+        roofline("stage_v_kernel", "stage_v_kernel<128>", wp.name, "hbm", vt_bytes,
+                 ms["stage_v"]),
+        rl_dec,
+        roofline("decode_combine_kernel", "decode_combine_kernel<128>", wd.name, "hbm",
+                 comb_bytes, ms["combine"]),
+    ]
 
     res = {
         "metric": METRIC,
@@ -258,23 +361,18 @@ def main():
                    "step": "prefill(B4 H16 L4096 d128) + decode(B64 H16 Lkv8192 d128)"},
         "prefill": {"ms": round(pre_ms, 4), "tflops": round(value, 2),
                     "frac_of_peak": round(value / PEAK_MFMA_BF16_TFLOPS, 4),
-                    "kernels_ms": {"stage_v": round(ms["stage_v"], 4),
-                                   "attend": round(ms["attend"], 4)},
+                    "step_ms": stats(pre_steps),
+                    "kernels_ms": {"stage_v": st["stage_v"], "attend": st["attend"]},
                     "flops": flops},
-        "roofline": {"kernel": "prefill_bf16_kernel<128>", "bound": "mfma",
-                     "achieved": round(att_tf, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(att_tf / PEAK_MFMA_BF16_TFLOPS, 4),
-                     "traffic": t_att},
+        "roofline": {k: v for k, v in rl_att.items() if k != "workload"},
         "decode": {"workload": wd.name, "ms": round(dec_ms, 4),
                    "value": round(dbytes / (dec_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                    "frac_of_peak": round(dbytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                   "split_keys": C, "bytes": dbytes,
-                   "kernels_ms": {"partials": round(ms["partials"], 4),
-                                  "combine": round(ms["combine"], 4)},
-                   "roofline": {"kernel": "decode_split_kernel<bf16,128>", "bound": "hbm",
-                                "achieved": round(part_gbs, 1), "peak": PEAK_HBM_GBS,
-                                "unit": "GB/s", "frac": round(part_gbs / PEAK_HBM_GBS, 4),
-                                "traffic": t_dec}},
+                   "split_keys": C, "bytes": dbytes, "step_ms": stats(dec_steps),
+                   "kernels_ms": {"partials": st["partials"], "combine": st["combine"]},
+                   "roofline": {k: v for k, v in rl_dec.items() if k != "workload"}},
+        "rooflines": rooflines,
+        "checksums": sums,
     }
 
     if args.calib_copy_mib:
@@ -297,20 +395,27 @@ def main():
         log("softmax-relative timing: workloads 2 and 3")
         rel.append(softmax_relative_prefill(torch, plx, wl, pin, wp, vt, pout))
         rel.append(softmax_relative_decode(torch, plx, wl, din, wd))
-    if not args.no_extra:
-        res["extra"], rel_extra, bwd_extra = extra_workloads(torch, plx, wl, dev,
-                                                             softmax=not args.no_softmax,
-                                                             backward=not args.no_backward)
-        if bwd_extra:
-            res["backward"].append(bwd_extra)
-        rel += rel_extra
-    if rel:
-        res["softmax_relative"] = rel
-
+    cpu = None
     if not args.no_cpu:
         log("cpu baseline")
-        res["cpu_baseline"] = cpu_baseline_prefill(pin, wp)
+        cpu = cpu_baseline_prefill(pin, wp)
         res["decode"]["cpu_baseline"] = cpu_baseline_decode(din, wd)
+    del pin, din, vt, pout, part, dout
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        res["extra"], rel_extra, bwd_extra, rl_extra, sums_extra = extra_workloads(
+            torch, plx, wl, dev, softmax=not args.no_softmax, backward=not args.no_backward)
+        if bwd_extra:
+            res.setdefault("backward", []).append(bwd_extra)
+        rel += rel_extra
+        res["rooflines"] += rl_extra
+        res["checksums"].update(sums_extra)
+    if rel:
+        res["softmax_relative"] = rel
+    if not args.no_sweep and not args.no_softmax:
+        res["softmax_sweep"] = softmax_sweep(torch, plx, wl, dev)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 
@@ -353,8 +458,8 @@ def chunk_block(torch, plx, wl, name, dev, steps=10):
     nb = wl.chunk_bytes(ctx, n, H, d)
     split = plx.chunk_default_split(B, H, Lmax, mq, d)
     res = {"workload": name, "split_keys": split if split < Lmax else None,
-           "ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 2),
-           "GB/s": round(nb / ms / 1e6, 1),
+           "ms": round(ms, 4), "ms_stats": tm.stats("chunk", 2),
+           "TFLOP/s": round(fl / ms / 1e9, 2), "GB/s": round(nb / ms / 1e6, 1),
            "staged_cache": {"ms": round(ms_st, 4), "TFLOP/s": round(fl / ms_st / 1e9, 2),
                             "GB/s": round(nb / ms_st / 1e6, 1)},
            "flops": fl, "bytes": nb}
@@ -394,7 +499,8 @@ def backward_block(torch, plx, wl, inp, w, steps=10):
     f_ms, b_ms = tm.ms("fwd", 2), tm.ms("bwd", 2)
     fl = wl.prefill_flops(B, H, L, d)
     return {"workload": w.name, "train_forward_ms": round(f_ms, 4),
-            "backward_ms": round(b_ms, 4), "step_ms": round(f_ms + b_ms, 4),
+            "backward_ms": round(b_ms, 4), "backward_ms_stats": tm.stats("bwd", 2),
+            "step_ms": round(f_ms + b_ms, 4),
             "train_forward_TFLOP/s": round(fl / f_ms / 1e9, 2),
             "backward_TFLOP/s": round(2 * fl / b_ms / 1e9, 2),
             "backward_frac_of_mfma_peak": round(2 * fl / b_ms / 1e9 / PEAK_MFMA_BF16_TFLOPS, 4),
@@ -426,7 +532,7 @@ def softmax_relative_prefill(torch, plx, wl, inp, w, vt, pout, steps=10):
 def softmax_relative_decode(torch, plx, wl, inp, w, steps=10):
     """Parallax decode step against the softmax-only decode step (split pass and
     combine each, same split size and workspace), alternating launch by launch."""
-    B, H, Lmax, d = w.B, w.H, w.Lmax, w.d
+    B, H, Lmax, d = inp["kcache"].shape
     C = plx.decode_default_split(B, H, Lmax, d)
     ws = torch.empty(plx.decode_workspace_bytes(B, H, Lmax, d, C), dtype=torch.uint8,
                      device=inp["q"].device)
@@ -443,19 +549,69 @@ def softmax_relative_decode(torch, plx, wl, inp, w, steps=10):
     pa, sm = tm.ms("parallax", 2), tm.ms("softmax", 2)
     nb = wl.decode_bytes(inp["seqlens"].tolist(), H, d)
     nb_sm = nb - B * H * d * 2 - 4 * H          # no rho, no gate
-    return {"workload": w.name, "kind": "decode", "split_keys": C,
+    return {"workload": w.name if w is not None else f"decode_bf16_B{B}_H{H}_L{Lmax}_d{d}",
+            "kind": "decode", "split_keys": C,
             "parallax_ms": round(pa, 4), "softmax_ms": round(sm, 4),
             "time_ratio": round(pa / sm, 4),
             "parallax_GB/s": round(nb / pa / 1e6, 1), "softmax_GB/s": round(nb_sm / sm / 1e6, 1),
             "bytes": {"parallax": nb, "softmax": nb_sm}}
 
 
+def softmax_sweep(torch, plx, wl, dev, steps=3):
+    """The pages' comparison with softmax attention across batch sizes and
+    context lengths: the Parallax kernels and their softmax-only twins on a grid
+    of shapes, alternating launch by launch (median of `steps` launches each
+    after one warm-up).  Prefill: H 16, L 1k-64k with B = max(1, 16k / L), at
+    d 64 and 128 (attend kernels; V staged once).  Decode: H 16, d 128,
+    B 1 / 8 / 64 x L 8k / 32k / 128k (split pass + combine)."""
+    pts = []
+    for d in (64, 128):
+        for L in (1024, 4096, 16384, 65536):
+            B = max(1, 16384 // L)
+            log(f"sweep: prefill B{B} H16 L{L} d{d}")
+            inp = wl.prefill_inputs(B, 16, L, d, "bf16", seed=3000 + L + d, device=dev,
+                                    rho_std=0.1, gate=("uniform", 0.2, 1.0))
+            vt = plx.prefill_stage_v(inp["v"])
+            out = torch.empty((B, 16, L, d), dtype=torch.float32, device=dev)
+            tm = Timer(torch)
+            for _ in range(steps + 1):
+                tm.run("parallax", lambda: plx.prefill_attend(inp["q"], inp["k"], vt, inp["rho"],
+                                                              inp["gate"], out=out))
+                tm.run("softmax", lambda: plx.softmax_prefill_attend(inp["q"], inp["k"], vt,
+                                                                     out=out))
+            torch.cuda.synchronize()
+            pa, sm = tm.ms("parallax", 1), tm.ms("softmax", 1)
+            fl = wl.prefill_flops(B, 16, L, d)
+            pts.append({"kind": "prefill", "B": B, "H": 16, "L": L, "d": d,
+                        "parallax_ms": round(pa, 4), "softmax_ms": round(sm, 4),
+                        "time_ratio": round(pa / sm, 4),
+                        "parallax_TFLOP/s": round(fl / pa / 1e9, 1),
+                        "softmax_TFLOP/s": round(fl / 2 / sm / 1e9, 1)})
+            del inp, vt, out
+            torch.cuda.empty_cache()
+    for L in (8192, 32768, 131072):
+        for B in (1, 8, 64):
+            log(f"sweep: decode B{B} H16 L{L} d128")
+            inp = wl.decode_inputs(B, 16, L, 128, "bf16", seed=3100 + B, device=dev,
+                                   rho_std=0.1)
+            r = softmax_relative_decode(torch, plx, wl, inp, None, steps=steps)
+            pts.append({"kind": "decode", "B": B, "H": 16, "L": L, "d": 128,
+                        "split_keys": r["split_keys"],
+                        "parallax_ms": r["parallax_ms"], "softmax_ms": r["softmax_ms"],
+                        "time_ratio": r["time_ratio"], "parallax_GB/s": r["parallax_GB/s"],
+                        "softmax_GB/s": r["softmax_GB/s"]})
+            del inp
+            torch.cuda.empty_cache()
+    return pts
+
+
 def extra_workloads(torch, plx, wl, dev, steps=10, softmax=True, backward=True):
     """Long ragged decode (B8 H16, 65536..131072 keys) and the d=64 prefill."""
-    out, rel, bwd = [], [], None
+    out, rel, bwd, rls, sums = [], [], None, [], {}
     w4 = wl.WORKLOADS[4]
     log("extra: decode workload 4")
     din = wl.make_workload(4, device=dev)
+    sums[w4.name] = checksums(din)
     C = plx.decode_default_split(w4.B, w4.H, w4.Lmax, w4.d)
     S = -(-w4.Lmax // C)
     part = torch.empty((w4.B, w4.H, S, 2 * w4.d + 4), dtype=torch.float32, device=dev)
@@ -469,10 +625,18 @@ def extra_workloads(torch, plx, wl, dev, steps=10, softmax=True, backward=True):
                                                      w4.Lmax, C, out=dout))
     torch.cuda.synchronize()
     nb = wl.decode_bytes(din["seqlens"].tolist(), w4.H, w4.d)
-    ms = tm.ms("partials", 2) + tm.ms("combine", 2)
+    ms = _median([a + b for a, b in zip(tm.times("partials", 2), tm.times("combine", 2))])
+    n_rec = sum(-(-min(int(x), w4.Lmax) // C) for x in din["seqlens"].tolist()) * w4.H
     out.append({"workload": w4.name, "ms": round(ms, 4), "GB/s": round(nb / ms / 1e6, 1),
                 "frac_of_hbm_peak": round(nb / ms / 1e6 / PEAK_HBM_GBS, 4), "bytes": nb,
-                "seqlens": din["seqlens"].tolist(), "split_keys": C})
+                "seqlens": din["seqlens"].tolist(), "split_keys": C,
+                "kernels_ms": {"partials": tm.stats("partials", 2),
+                               "combine": tm.stats("combine", 2)}})
+    rls.append(roofline("decode_split_kernel", "decode_split_kernel<bf16,128>", w4.name, "hbm",
+                        nb, tm.ms("partials", 2)))
+    rls.append(roofline("decode_combine_kernel", "decode_combine_kernel<128>", w4.name, "hbm",
+                        n_rec * (2 * w4.d + 4) * 4 + w4.B * w4.H * w4.d * 4,
+                        tm.ms("combine", 2)))
     del part, dout
     if softmax:
         log("softmax-relative timing: workload 4")
@@ -483,6 +647,7 @@ def extra_workloads(torch, plx, wl, dev, steps=10, softmax=True, backward=True):
     w5 = wl.WORKLOADS[5]
     log("extra: prefill workload 5")
     pin = wl.make_workload(5, device=dev)
+    sums[w5.name] = checksums(pin)
     vt = torch.empty(plx.prefill_workspace_bytes(w5.B, w5.H, w5.L, w5.d), dtype=torch.uint8,
                      device=dev)
     pout = torch.empty((w5.B, w5.H, w5.L, w5.d), dtype=torch.float32, device=dev)
@@ -494,12 +659,18 @@ def extra_workloads(torch, plx, wl, dev, steps=10, softmax=True, backward=True):
     torch.cuda.synchronize()
     fl = wl.prefill_flops(w5.B, w5.H, w5.L, w5.d)
     ms_a = tm.ms("attend", 2)
-    ms = tm.ms("stage_v", 2) + ms_a
+    ms = _median([a + b for a, b in zip(tm.times("stage_v", 2), tm.times("attend", 2))])
     out.append({"workload": w5.name, "ms": round(ms, 4),
                 "TFLOP/s": round(fl / ms / 1e9, 2),
                 "frac_of_mfma_peak": round(fl / ms / 1e9 / PEAK_MFMA_BF16_TFLOPS, 4),
-                "attend_ms": round(ms_a, 4),
-                "attend_TFLOP/s": round(fl / ms_a / 1e9, 2), "flops": fl})
+                "attend_ms": round(ms_a, 4), "attend_TFLOP/s": round(fl / ms_a / 1e9, 2),
+                "kernels_ms": {"stage_v": tm.stats("stage_v", 2),
+                               "attend": tm.stats("attend", 2)},
+                "flops": fl})
+    rls.append(roofline("prefill_bf16_kernel", "prefill_bf16_kernel<64>", w5.name, "mfma", fl,
+                        ms_a))
+    rls.append(roofline("stage_v_kernel", "stage_v_kernel<64>", w5.name, "hbm",
+                        2 * w5.B * w5.H * w5.L * w5.d * 2, tm.ms("stage_v", 2)))
     if softmax:
         log("softmax-relative timing: workload 5")
         rel.append(softmax_relative_prefill(torch, plx, wl, pin, w5, vt, pout))
@@ -509,7 +680,7 @@ def extra_workloads(torch, plx, wl, dev, steps=10, softmax=True, backward=True):
         bwd = backward_block(torch, plx, wl, pin, w5)
     del pin
     torch.cuda.empty_cache()
-    return out, rel, bwd
+    return out, rel, bwd, rls, sums
 
 
 if __name__ == "__main__":
