@@ -32,8 +32,10 @@
  *     the call returns an error status, enqueues nothing and sets the text of
  *     parallax_last_error().  A failed launch or allocation returns PLX_EHIP /
  *     PLX_ENOMEM.  The library never aborts, prints or throws across the ABI.
- *   - Apart from the per-thread error text the library has no mutable global
- *     state; calls from several host threads are safe.
+ *   - Apart from the per-thread error text and the per-device address of the
+ *     scratch array of parallax_decode_noalloc (looked up once per device,
+ *     under a once-flag), the library has no mutable global state; calls from
+ *     several host threads are safe.
  */
 #ifndef PARALLAX_H
 #define PARALLAX_H
@@ -45,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 6
+#define PARALLAX_ABI_VERSION 7
 
 typedef enum {
   PLX_OK = 0,
@@ -155,6 +157,29 @@ int parallax_decode_combine(const float* partials, const float* gate, const int3
 
 /* The split size parallax_decode uses when split_keys is 0. */
 int parallax_decode_default_split(int B, int H, int Lmax, int d);
+
+/* parallax_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * takes no workspace and calls no allocator: the split records live in a
+ * fixed scratch array that the library's code object carries on every device
+ * it runs on (parallax_decode_noalloc_max_bytes() bytes, 32 MiB, held until
+ * the process ends).  Its device address is looked up once per device, on the
+ * first call with that device current.  Arguments, layouts and results are
+ * those of parallax_decode, which it matches bit for bit at the same
+ * split_keys.  A call whose records
+ * (parallax_decode_workspace_bytes(B, H, Lmax, d, split_keys)) exceed the
+ * scratch returns PLX_EINVAL without enqueuing anything: pass a larger
+ * split_keys.  The scratch is shared by every call on the same device and
+ * keeps the last call's records; calls that overlap in time on one device
+ * (different streams or host threads) race on it and must be ordered by the
+ * caller.  The calling thread's current device must be the device of
+ * `stream`. */
+size_t parallax_decode_noalloc_max_bytes(void);
+
+int parallax_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                            const void* rho, const float* gate, float* out,
+                            const int32_t* seqlens, int B, int H, int Lmax, int d, float scale,
+                            int dtype, int split_keys, void* stream);
 
 /* ----------------------------------------------------------- chunked prefill
  * The step between prefill and decode (the pages' kernels target every batch

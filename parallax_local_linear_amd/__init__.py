@@ -373,6 +373,26 @@ def decode(q, kcache, vcache, rho, gate, seqlens, scale=None, split_keys=0, out=
     return out
 
 
+def decode_noalloc(q, kcache, vcache, rho, gate, seqlens, scale=None, split_keys=0, out=None):
+    """decode through parallax_decode_noalloc: no workspace, the split records
+    go to the library's fixed per-device scratch.  `out` must be given by a
+    caller that allocates nothing per call."""
+    B, H, Lmax, d, dt = _decode_checks(q, kcache, vcache, rho, seqlens)
+    _check("gate", gate, torch.float32, (H,), q.device)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    _check("out", out, torch.float32, (B, H, d), q.device)
+    _launch(q.device, "parallax_decode_noalloc", _ptr(q), _ptr(kcache), _ptr(vcache), _ptr(rho),
+            _ptr(gate), _ptr(out), _ptr(seqlens), B, H, Lmax, d, _scale(scale, d), _DT[dt],
+            int(split_keys))
+    return out
+
+
+def decode_noalloc_max_bytes():
+    """Bytes of split records parallax_decode_noalloc can hold."""
+    return int(lib().parallax_decode_noalloc_max_bytes())
+
+
 def softmax_decode(q, kcache, vcache, seqlens, scale=None, split_keys=0, out=None,
                    workspace=None):
     """One softmax-attention decode step through the decode kernels with the

@@ -34,6 +34,8 @@ SIGNATURES = {
                                       _i, _vp]),
     "parallax_decode_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "parallax_decode_default_split": (_i, [_i, _i, _i, _i]),
+    "parallax_decode_noalloc_max_bytes": (_sz, []),
+    "parallax_decode_noalloc": (_i, [_vp] * 7 + [_i, _i, _i, _i, _f, _i, _i, _vp]),
     "parallax_softmax_prefill": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _sz,
                                       _vp]),
     "parallax_softmax_prefill_attend": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp]),

@@ -16,7 +16,8 @@ import time
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libparallax.so")
-SOURCES = ["api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "backward.hip"]
+SOURCES = ["api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "backward.hip",
+           "noalloc_scratch.hip"]
 ARCH = os.environ.get("PLX_OFFLOAD_ARCH", "gfx950")
 
 

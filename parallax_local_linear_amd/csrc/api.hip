@@ -45,6 +45,8 @@ int chunk_num_splits(int Lmax, int split_keys);
 size_t chunk_part_bytes(int T, int H, int Lmax, int d, int split_keys);
 bool chunk_fuses_v(int d, int max_q);
 long long chunk_split_blocks(int B, int H, int Lmax, int max_q, int d, int split_keys);
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_stage_v_rows(const void* vc, void* vt, const int* cu_q, const int* ctx, int B,
                                int H, int T, int Lmax, int max_q, int d, bool new_rows_only,
                                hipStream_t s);
@@ -374,6 +376,41 @@ int parallax_decode(const void* q, const void* kcache, const void* vcache, const
   return decode_impl("parallax_decode", q, kcache, vcache, rho, gate, out, seqlens, B, H, Lmax,
                      d, scale, dtype, split_keys, workspace, workspace_bytes,
                      (hipStream_t)stream, true);
+}
+
+size_t parallax_decode_noalloc_max_bytes(void) { return plx::noalloc_scratch_bytes(); }
+
+int parallax_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                            const void* rho, const float* gate, float* out,
+                            const int32_t* seqlens, int B, int H, int Lmax, int d, float scale,
+                            int dtype, int split_keys, void* stream) {
+  const char* fn = "parallax_decode_noalloc";
+  int st = PLX_OK;
+  if (!dims_ok(B, H, Lmax, d, fn, "Lmax", &st)) return st;
+  if (!streams_ok(B, H, fn, &st)) return st;
+  if (!dtype_ok(dtype, fn, &st)) return st;
+  if (split_keys < 0) return fail(PLX_EINVAL, "%s: split_keys must be >= 0", fn);
+  const int C = split_keys > 0 ? split_keys : default_split(B, H, Lmax);
+  if (!split_ok(C, fn, &st)) return st;
+  if (!q || !kcache || !vcache || !rho || !gate || !out || !seqlens)
+    return fail(PLX_EINVAL, "%s: null pointer", fn);
+  const size_t need = part_bytes(B, H, Lmax, d, C);
+  if (need > plx::noalloc_scratch_bytes())
+    return fail(PLX_EINVAL,
+                "%s: the split records need %zu bytes, more than the %zu-byte scratch; pass a "
+                "larger split_keys or call parallax_decode with a workspace",
+                fn, need, plx::noalloc_scratch_bytes());
+  void* ws = nullptr;
+  hipError_t se = plx::noalloc_scratch(&ws);
+  if (se != hipSuccess) return hip_fail("parallax_decode_noalloc: scratch address", se);
+  hipStream_t s = (hipStream_t)stream;
+  float* part = static_cast<float*>(ws);
+  hipError_t e = plx::launch_decode_split(q, kcache, vcache, rho, seqlens, part, B, H, Lmax, d,
+                                          C, eff_scale(scale, d), dtype == PLX_BF16, true, s);
+  if (e != hipSuccess) return launch_fail(fn, "split", e);
+  e = plx::launch_decode_combine(part, gate, seqlens, out, B, H, Lmax, d, C, true, s);
+  if (e != hipSuccess) return launch_fail(fn, "combine", e);
+  return ok();
 }
 
 int parallax_softmax_prefill(const void* q, const void* k, const void* v, float* out, int B,

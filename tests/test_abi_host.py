@@ -95,6 +95,22 @@ def test_decode_rejects_bad_arguments(lib):
     assert h(x, x, x, NULL, 1, 1, 64, 128, 64, NULL) == PLX_EINVAL
 
 
+def test_decode_noalloc_rejects_bad_arguments(lib):
+    x = ctypes.c_void_p(0x1000)
+    f = lib.parallax_decode_noalloc
+    assert lib.parallax_decode_noalloc_max_bytes() == 32 << 20
+    assert f(x, x, x, x, x, x, NULL, 1, 1, 64, 128, 0.0, 1, 0, NULL) == PLX_EINVAL
+    assert f(x, x, x, x, x, x, x, 1, 1, 64, 80, 0.0, 1, 0, NULL) == PLX_EUNSUPPORTED
+    assert f(x, x, x, x, x, x, x, 1, 1, 64, 128, 0.0, 1, 100, NULL) == PLX_EINVAL
+    assert f(x, x, x, x, x, x, x, 1, 1, 64, 128, 0.0, 3, 0, NULL) == PLX_EUNSUPPORTED
+    # records beyond the fixed scratch are refused in validation, before any HIP call
+    B, H, Lmax, d = 64, 16, 131072, 128
+    assert lib.parallax_decode_workspace_bytes(B, H, Lmax, d, 64) > \
+        lib.parallax_decode_noalloc_max_bytes()
+    assert f(x, x, x, x, x, x, x, B, H, Lmax, d, 0.0, 1, 64, NULL) == PLX_EINVAL
+    assert b"scratch" in lib.parallax_last_error()
+
+
 def test_softmax_calls_reject_bad_arguments(lib):
     x = ctypes.c_void_p(0x1000)
     f = lib.parallax_softmax_prefill
