@@ -127,9 +127,10 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int r0, int f0, 
   const int c = (f0 >> 3) + ((c16 & 3) >> 1);    // logical chunk of features f0 + 4 (c16 & 3)
   const int e = 4 * (c16 & 1);                   // their first element within the chunk
   const int r = r0 + 4 * g4 + (c16 >> 2);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + rm_off<D>(r, c) + e));
-  const s16x4 hi =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + rm_off<D>(r + 16, c) + e));
+  // rm_swz repeats every 16 rows: the second block is the same offset 16 rows on
+  const uint16_t* p = tile + rm_off<D>(r, c) + e;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * D));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -355,9 +356,9 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   };
 
   // MASK: the step holds a query before one of this wave's keys, or past L
-  auto compute = [&](int qs, int buf, auto mask_c) {
+  auto compute = [&](int qs, auto par, auto mask_c) {
     constexpr bool MASK = decltype(mask_c)::value;
-    const uint16_t* st = smem + buf * STAGE;
+    const uint16_t* st = smem + decltype(par)::value * STAGE;
     const uint16_t* Qs = st;
     const uint16_t* Rs = st + RM;
     const uint16_t* Os = st + 2 * RM;
@@ -367,24 +368,21 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     // holds key kw0 + 16 kb + c16 and queries q0 + 16 qb + 4 g4 + j
     f32x4 sa[KB][2], ra[KB][2], da[KB][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int kk = 0; kk < KSTEPS; ++kk) {
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        const int off = rm_off<D>(16 * qb + c16, 4 * kk + g4);
+      for (int qb = 0; qb < 2; ++qb) {
+        const int off = rm_off<D>(c16, 4 * kk + g4) + 16 * qb * D;   // rm_swz repeats every 16 rows
         const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qs + off);
         const bf16x8 ar = *reinterpret_cast<const bf16x8*>(Rs + off);
         const bf16x8 ao = *reinterpret_cast<const bf16x8*>(Os + off);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          if (kk == 0) {
-            sa[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kf[kb][0], f32x4{}, 0, 0, 0);
-            ra[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, kf[kb][0], f32x4{}, 0, 0, 0);
-            da[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, vf[kb][0], f32x4{}, 0, 0, 0);
-          } else {
-            sa[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kf[kb][kk], sa[kb][qb], 0, 0, 0);
-            ra[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, kf[kb][kk], ra[kb][qb], 0, 0, 0);
-            da[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, vf[kb][kk], da[kb][qb], 0, 0, 0);
-          }
+          const f32x4 zs = kk == 0 ? f32x4{} : sa[kb][qb];
+          const f32x4 zr = kk == 0 ? f32x4{} : ra[kb][qb];
+          const f32x4 zd = kk == 0 ? f32x4{} : da[kb][qb];
+          sa[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kf[kb][kk], zs, 0, 0, 0);
+          ra[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, kf[kb][kk], zr, 0, 0, 0);
+          da[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, vf[kb][kk], zd, 0, 0, 0);
         }
       }
     }
@@ -430,19 +428,24 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
-  for (int qs = qs0; qs < n_qs; ++qs) {
-    const int buf = (qs - qs0) & 1;
+  // step qs reads buffer P = (qs - qs0) & 1, a compile-time parity
+  auto step = [&](int qs, auto par) {
+    constexpr int P = decltype(par)::value;
     // staging is unconditional: past the last step the loads re-read it into
     // the buffer no wave reads again
-    load_stage(min(qs + 1, n_qs - 1), 1 - buf);
+    load_stage(min(qs + 1, n_qs - 1), 1 - P);
     // a wave whose keys all follow the step's last query has nothing to add
     const int q0 = qs * BW_BQ;
     if (q0 + BW_BQ - 1 >= kw0) {
-      if (q0 < kw0 + 16 * KB || q0 + BW_BQ > L) compute(qs, buf, std::true_type{});
-      else compute(qs, buf, std::false_type{});
+      if (q0 < kw0 + 16 * KB || q0 + BW_BQ > L) compute(qs, par, std::true_type{});
+      else compute(qs, par, std::false_type{});
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+  };
+  for (int qs = qs0; qs < n_qs; qs += 2) {
+    step(qs, std::integral_constant<int, 0>{});
+    if (qs + 1 < n_qs) step(qs + 1, std::integral_constant<int, 1>{});
   }
 
 #pragma unroll
@@ -550,8 +553,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       buffer_load_lds16(kts, TE * 2, st + 2 * TE + (i * NW + wave_u) * 512, troff[i]);
   };
 
-  auto compute = [&](int kt, int buf, auto diag_c) {
-    const uint16_t* st = smem + buf * STAGE;
+  auto compute = [&](int kt, auto par, auto diag_c) {
+    const uint16_t* st = smem + decltype(par)::value * STAGE;
     const uint16_t* Ks = st;
     const uint16_t* Vs = st + TE;
     const uint16_t* KTs = st + 2 * TE;
@@ -605,15 +608,19 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   load_stage(0, 0);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    load_stage(min(kt + 1, n_kt - 1), 1 - buf);
+  // tile kt reads buffer kt & 1, a compile-time parity
+  auto step = [&](int kt, auto par) {
+    load_stage(min(kt + 1, n_kt - 1), 1 - decltype(par)::value);
     if (kt < n_w) {
-      if (kt + 1 == n_w) compute(kt, buf, std::true_type{});
-      else compute(kt, buf, std::false_type{});
+      if (kt + 1 == n_w) compute(kt, par, std::true_type{});
+      else compute(kt, par, std::false_type{});
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+  };
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < n_kt) step(kt + 1, std::integral_constant<int, 1>{});
   }
 
   if (qi < L) {
