@@ -119,39 +119,76 @@ def test_backward_deterministic():
         assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("wid", [2, 5])
-def test_backward_full_workload_sampled(wid):
-    """The full-size bf16 workloads: every gradient element of sampled heads
-    against the oracle, and the gate gradient of one head (summed over the
-    batch) for workload 2."""
+_FULL = {}
+
+
+def _full_backward(wid):
+    """Gradients of a full-size bf16 workload in the benchmark's launch
+    configuration, with fp64 host copies of the inputs, made once per session."""
+    if wid not in _FULL:
+        _FULL.clear()
+        torch.cuda.empty_cache()
+        w = wl.WORKLOADS[wid]
+        inp = wl.make_workload(wid, device="cuda")
+        dout = _dout((w.B, w.H, w.L, w.d), 980 + wid)
+        _, grads = _run(inp, dout)
+        for t in grads:
+            assert bool(torch.isfinite(t).all())
+        _FULL[wid] = dict(
+            h={n: inp[n].double().cpu().numpy() for n in ("q", "k", "v", "rho", "gate")},
+            dout=dout.double().cpu().numpy(),
+            grads=[t.cpu().numpy() for t in grads])
+        del inp, dout, grads
+        torch.cuda.empty_cache()
+    return _FULL[wid]
+
+
+def _check_heads(wid, heads, check_dgate=()):
+    """Every gradient element of the given (b, h) heads against the oracle, and
+    dgate[h] (summed over the batch) for the heads h in check_dgate, whose every
+    batch entry must be among `heads`."""
     w = wl.WORKLOADS[wid]
-    inp = wl.make_workload(wid, device="cuda")
-    dout = _dout((w.B, w.H, w.L, w.d), 980 + wid)
-    _, grads = _run(inp, dout)
-    for t in grads:
-        assert bool(torch.isfinite(t).all())
-    heads = [(0, 0), (w.B - 1, w.H - 1)] if wid == 2 else [(w.B - 1, 5)]
-    if wid == 2:
-        heads += [(b, 0) for b in range(1, w.B)]
+    st = _full_backward(wid)
+    h, grads = st["h"], st["grads"]
     worst = {n: 0.0 for n in GRADS}
-    dg0 = 0.0
+    dg = {hh: 0.0 for hh in check_dgate}
     for b, hh in heads:
-        x = {n: inp[n][b, hh].double().cpu().numpy() for n in ("q", "k", "v", "rho")}
-        g = float(inp["gate"][hh])
-        ref = po.prefill_head_backward(x["q"], x["k"], x["v"], x["rho"], g, w.scale,
-                                       dout[b, hh].double().cpu().numpy())
-        for n, t, r in zip(GRADS, grads[:4], ref[:4]):
-            worst[n] = max(worst[n], _rel_err(_np(t[b, hh]), r))
-        if hh == 0:
-            dg0 += ref[4]
-        print(f"workload {wid} head ({b},{hh}): " + " ".join(f"{n} {e:.2e}" for n, e in worst.items()),
+        ref = po.prefill_head_backward(h["q"][b, hh], h["k"][b, hh], h["v"][b, hh],
+                                       h["rho"][b, hh], float(h["gate"][hh]), w.scale,
+                                       st["dout"][b, hh])
+        errs = {n: _rel_err(t[b, hh], r) for n, t, r in zip(GRADS, grads[:4], ref[:4])}
+        for n, e in errs.items():
+            worst[n] = max(worst[n], e)
+        if hh in dg:
+            dg[hh] += ref[4]
+        print(f"workload {wid} head ({b},{hh}): " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()),
               flush=True)
     for n, e in worst.items():
         assert e <= 2e-2, n
-    if wid == 2:
-        e = abs(float(grads[4][0]) - dg0) / max(1.0, abs(dg0))
-        print(f"workload 2 dgate[0]: {float(grads[4][0]):.6e} vs {dg0:.6e} (rel {e:.2e})", flush=True)
+    for hh, ref in dg.items():
+        e = abs(float(grads[4][hh]) - ref) / max(1.0, abs(ref))
+        print(f"workload {wid} dgate[{hh}]: {float(grads[4][hh]):.6e} vs {ref:.6e} (rel {e:.2e})",
+              flush=True)
         assert e <= 2e-2
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_backward_workload2_every_head(part):
+    """Workload 2 (B4 H16 L4096 d128): every gradient element of all 64 heads and
+    dgate of every head, four heads (all batch entries) per test."""
+    w = wl.WORKLOADS[2]
+    hs = range(4 * part, 4 * part + 4)
+    _check_heads(2, [(b, hh) for hh in hs for b in range(w.B)], check_dgate=hs)
+
+
+@pytest.mark.parametrize("part", range(8))
+def test_backward_workload5_every_head(part):
+    """Workload 5 (B2 H32 L16384 d64, duplicated key runs): every gradient element
+    of all 64 heads, eight per test (about 2 s of oracle time per head on 16
+    cores), and dgate of the four heads whose both batch entries a test holds."""
+    w = wl.WORKLOADS[5]
+    hs = range(4 * part, 4 * part + 4)
+    _check_heads(5, [(b, hh) for hh in hs for b in range(w.B)], check_dgate=hs)
 
 
 def test_autograd_function_matches_the_oracle():
