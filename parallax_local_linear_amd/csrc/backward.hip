@@ -266,8 +266,11 @@ __device__ __forceinline__ void bwd_grid_order(int b, int BH, int n_t, int* t, i
   }
 }
 
+// At least two waves per SIMD (8 waves per CU): with four-wave workgroups the
+// bound asks for two workgroups, which keeps the compiler from trading
+// occupancy for accumulator registers (AGPRs).
 template <int D, int NW, int KB>
-__global__ __launch_bounds__(64 * NW, 1)
+__global__ __launch_bounds__(64 * NW, 8 / NW)
 void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, const __bf16* __restrict__ rho,
                      const __bf16* __restrict__ do16, const f32x4* __restrict__ stats,
