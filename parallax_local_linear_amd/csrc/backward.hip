@@ -17,9 +17,8 @@
 // Kernels (one stream, in this order):
 //   bwd_prep_kernel   dO -> bf16 (row-major copy), per-row constants of the
 //                     elementwise step and per-tile partials of <dO, C>.
-//   stage_v_kernel    (bf16 output) transposed 64-row tiles of dO, Q, rho and K
-//                     with the rows of each 32-row group in the order in which a
-//                     lane group of the score MFMAs produces them.
+//   stage_v_kernel    (bf16 output) transposed 64-key tiles of K, the K^T
+//                     operand of the query-stationary kernel.
 //   bwd_dkdv_kernel   key-stationary: a workgroup owns 16*KB*NW keys, each wave
 //                     16*KB of them with their K and V fragments in registers;
 //                     it streams the later queries through LDS in steps of 32
@@ -43,6 +42,11 @@ constexpr int BW_T = 64;    // keys per tile of the query-stationary kernel (the
 constexpr int BW_BQ = 32;   // queries per step of the key-stationary kernel
 
 // Launch shapes (waves per workgroup, 16-key blocks per wave), per head dimension.
+// At d = 128 the key-stationary kernel is bound by LDS bandwidth: every wave
+// reads each step's query tiles twice (score fragments and transposed halves),
+// 56 KB of LDS reads per wave and 32-query step for 48 MFMAs.  Two 16-key blocks
+// per wave would halve that, but the dK and dV accumulators of 32 keys need 128
+// VGPRs and the kernel then no longer fits two waves per SIMD.
 // Grid order of the dK/dV and dQ kernels, per head dimension: 0 = the tiles of
 // all heads in order of work with heads fastest; G > 0 = the same within groups
 // of G heads, group after group (more tiles of fewer heads share each XCD's L2).
