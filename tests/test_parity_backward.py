@@ -234,6 +234,49 @@ def test_backward_partial_head_group(d):
         assert e <= 2e-2, n
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_many_heads(d):
+    """The widest backward grids: 4096 heads (B64 H64) of 100 rows, every
+    gradient element and dgate (summed over 64 batch entries) against the
+    oracle."""
+    B, H, L = 64, 64, 100
+    inp = wl.prefill_inputs(B, H, L, d, "bf16", seed=1700 + d, device="cuda", rho_std=0.5,
+                            gate=("uniform", 0.2, 1.0))
+    dout = _dout((B, H, L, d), 1800 + d)
+    _, grads = _run(inp, dout)
+    h = {n: inp[n].cpu() for n in inp}
+    ref = po.prefill_backward(h["q"], h["k"], h["v"], h["rho"], h["gate"], dout.cpu())
+    errs = {n: _rel_err(_np(t), ref[n]) for n, t in zip(GRADS, grads[:4])}
+    errs["dgate"] = _rel_err(_np(grads[4]), ref["dgate"])
+    print(f"backward 4096 heads d{d}: " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()),
+          flush=True)
+    for n, e in errs.items():
+        assert e <= 2e-2, n
+
+
+@pytest.mark.parametrize("d,L", [(128, 32768), (64, 65536)])
+def test_backward_long_sequence(d, L):
+    """One head of 32768 (d=128) or 65536 (d=64) rows: 256 or 1024 key blocks
+    of the key-stationary grid and the longest query-stationary rows, every
+    gradient element against the oracle."""
+    inp = wl.prefill_inputs(1, 1, L, d, "bf16", seed=1900 + d, device="cuda", rho_std=0.5,
+                            gate=("uniform", 0.2, 1.0))
+    dout = _dout((1, 1, L, d), 2000 + d)
+    _, grads = _run(inp, dout)
+    for t in grads:
+        assert bool(torch.isfinite(t).all())
+    h = {n: inp[n].double().cpu().numpy() for n in ("q", "k", "v", "rho", "gate")}
+    ref = po.prefill_head_backward(h["q"][0, 0], h["k"][0, 0], h["v"][0, 0], h["rho"][0, 0],
+                                   float(h["gate"][0]), d ** -0.5,
+                                   dout[0, 0].double().cpu().numpy())
+    errs = {n: _rel_err(_np(t[0, 0]), r) for n, t, r in zip(GRADS, grads[:4], ref[:4])}
+    errs["dgate"] = abs(float(grads[4][0]) - ref[4]) / max(1.0, abs(ref[4]))
+    print(f"backward L{L} d{d}: " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()),
+          flush=True)
+    for n, e in errs.items():
+        assert e <= 2e-2, n
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_backward_random_shapes(seed):
     """Seeded random shapes: B 1-2, H 1-36 (partial head groups), L 1-260, d 64
