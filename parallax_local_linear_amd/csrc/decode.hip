@@ -265,6 +265,31 @@ void decode_combine_kernel(const float* __restrict__ part, const float* __restri
   }
   const float* rec = part + (size_t)bh * S * RF;
 
+  // Thread (group sg, column cc) sums splits sg, sg + NSG, ... of feature
+  // column cc, UNR at a time, in split order.  Its first UNR splits are loaded
+  // before the stream's (M, l, c) is known, so that both rounds of record loads
+  // are in flight together.
+  const int cc = tid % NC, sg = tid / NC;
+  const bool col = cc < NF / 4;
+  constexpr int UNR = 8;
+  f32x4 v[UNR];
+  float w[UNR];
+  auto load = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int sp = s0 + u * NSG;
+      if (col && sp < ns) {
+        const float* r = rec + (size_t)sp * RF;
+        w[u] = r[0];
+        v[u] = *reinterpret_cast<const f32x4*>(r + 4 + 4 * cc);
+      } else {
+        w[u] = -INFINITY;
+        v[u] = f32x4{};
+      }
+    }
+  };
+  load(sg);
+
   // 1. (M, l, c) of the stream
   Mlc t{kMinit, 0.f, 0.f};
   for (int sp = tid; sp < ns; sp += 256) {
@@ -278,27 +303,14 @@ void decode_combine_kernel(const float* __restrict__ part, const float* __restri
   const Mlc tot = mlc_merge(mlc_merge(s_w[0], s_w[1]), mlc_merge(s_w[2], s_w[3]));
   const float M = tot.m;
 
-  // 2. weighted feature sums: thread (group sg, column cc)
-  const int cc = tid % NC, sg = tid / NC;
+  // 2. weighted feature sums
   f32x4 acc = {};
-  constexpr int UNR = 8;
-  for (int s0 = sg; cc < NF / 4 && s0 < ns; s0 += UNR * NSG) {
-    f32x4 v[UNR];
-    float w[UNR];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int sp = s0 + u * NSG;
-      if (sp < ns) {
-        const float* r = rec + (size_t)sp * RF;
-        w[u] = r[0];
-        v[u] = *reinterpret_cast<const f32x4*>(r + 4 + 4 * cc);
-      } else {
-        w[u] = -INFINITY;
-        v[u] = f32x4{};
-      }
-    }
+  for (int s0 = sg;;) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) acc += __builtin_amdgcn_exp2f(w[u] - M) * v[u];
+    s0 += UNR * NSG;
+    if (!col || s0 >= ns) break;
+    load(s0);
   }
   s_acc[sg][cc] = acc;
   __syncthreads();
