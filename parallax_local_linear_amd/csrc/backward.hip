@@ -281,6 +281,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const float* __restrict__ gate, float* __restrict__ dk,
                      float* __restrict__ dv, int H, int L, int BH,
                      int n_kblk, float sl2, float scale) {
+  static_assert(NW == 4 || NW == 8, "the launch bounds ask for 8 / NW workgroups per CU");
   constexpr int KSTEPS = D / 32;
   constexpr int FB = D / 16;
   constexpr int BK = 16 * KB * NW;                 // keys per workgroup
