@@ -36,6 +36,10 @@
 //   * The running max moves lazily: only when some row's tile max exceeds it by
 //     more than kRescaleSlack (log2 units), which makes the rescale of the
 //     accumulators rare after the first tile.
+//   * R has no bound (rho is an input).  The tile walk converts it to fp16
+//     unchecked; a row whose R or T overflowed fp16 ends with a non-finite c, and
+//     its wave then walks its keys once more with a per-tile range check that
+//     scales the row's R by a power of two (exact: Eq. 2 is linear in rho).
 //   * The register footprint stays within 256 per lane so that two waves share
 //     each SIMD and one wave's MFMAs overlap the other's softmax arithmetic.
 //   * Grid order: the longest (last) query tiles of every head first; heads
@@ -124,16 +128,16 @@ constexpr int kWaitLgkm0 = 0xC07F;
 // Rescale slack in log2 units: P = 2^(s - m) may grow to 2^kRescaleSlack before
 // the running max m is moved, so fp16 P <= 16.
 constexpr float kRescaleSlack = 4.0f;
-// Largest |R| a row may feed to the fp16 products: with P <= 16, T = P*R stays
-// below 2^15, inside fp16's range.  A row whose R exceeds it is scaled by a
-// power of two (exactly; Eq. 2 is linear in rho), see rescale_r.
+// Largest |R| a row may feed to the fp16 products in the checked pass: with
+// P <= 16, T = P*R stays below 2^15, inside fp16's range.  A row whose R exceeds
+// it is scaled by a power of two (exactly; Eq. 2 is linear in rho), see rescale_r.
 constexpr float kRMax = 2048.0f;
 static_assert(16.0f * kRMax < 65504.0f, "T = P*R must fit fp16");
 
 // LDS tiles have no padding; 16-byte chunks are XOR-swizzled by row instead,
 // which keeps every fragment read and tile store free of bank conflicts
-// (measured on gfx950: a conflict-free ds_read_b128 occupies the LDS for 4
-// cycles, while a 16-byte row padding still costs 8).
+// (measured on gfx950: a conflict-free ds_read_b128 occupies the LDS for 8
+// cycles, and twice as long with a 16-byte row padding).
 template <int D>
 struct PfLayout {
   static constexpr int KCHUNKS = D / 8;        // 16-byte chunks per K row
@@ -408,7 +412,30 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   };
   // this wave's tile loads have landed in LDS (then a barrier publishes them)
   auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); };
-  // S^T = K Q^T and R^T = K rho^T of one tile; lane holds keys 16*kb + 4*g4 + j
+  // S^T = K Q^T and R^T = K rho^T of one tile; lane holds keys 16*kb + 4*g4 + j.
+  // kfrag(kb, kk): the K fragment of key 16*kb + c16, features 32*kk + 8*g4 .. +7.
+  // The checked pass after the tile walk reads its fragments through this; the
+  // walk keeps its own copy with the LDS reads written out (`scores`), because
+  // routing them through the fragment functor changed the register allocation
+  // of the kernels that run at 250-256 VGPRs and made some of them spill.
+  auto scores_of = [&](auto kfrag, f32x4 (&sa)[4], f32x4 (&ra)[4]) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      bf16x8 a[KSTEPS];
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) a[kk] = kfrag(kb, kk);
+      sa[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], qf[0], f32x4{}, 0, 0, 0);
+      if constexpr (CORR)
+        ra[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], rf[0], f32x4{}, 0, 0, 0);
+#pragma unroll
+      for (int kk = 1; kk < KSTEPS; ++kk) {
+        sa[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], qf[kk], sa[kb], 0, 0, 0);
+        if constexpr (CORR)
+          ra[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], rf[kk], ra[kb], 0, 0, 0);
+      }
+    }
+  };
+  // the same with K tile `buf` in LDS
   auto scores = [&](auto buf, f32x4 (&sa)[4], f32x4 (&ra)[4]) {
     const uint16_t* ks = smem + (int)buf * LY::K_ELEMS;
 #pragma unroll
@@ -478,12 +505,17 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       for (int e = 0; e < 8; ++e) rf[kk][e] = (__bf16)((float)rf[kk][e] * f);
     }
   };
+  // The tile walk checks |R| per tile only with the in-kernel V conversion
+  // (FUSEV); the other kernels check each row once, after the walk (below).
+  using kHotCheck = std::integral_constant<bool, (FUSEV > 0)>;
   // Causal mask (the wave's last tile is its only diagonal tile) and the scaled
   // row max of one tile's scores; the four lanes that share a query combine.
   // With the correction, masked keys also get R = 0 (they never reach a row's
-  // sums, so their |R| must not steer its scale), and the tile's |R| is checked
-  // against kRMax before its fp16 conversion.
-  auto tile_max = [&](f32x4 (&sa)[4], f32x4 (&ra)[4], int kt_, auto diag_c) -> float {
+  // sums: neither their |R| nor an fp16 overflow of it may touch the row).  In
+  // the checked walk (`chk`) the tile's |R| is held to kRMax before its fp16
+  // conversion.
+  auto tile_max = [&](f32x4 (&sa)[4], f32x4 (&ra)[4], int kt_, auto diag_c,
+                      auto chk) -> float {
     if constexpr (decltype(diag_c)::value) {
       const int lim = pos0 + qi - kt_ * PF_BC - 4 * g4;   // key offset 16*kb + j kept iff <= lim
 #pragma unroll
@@ -503,7 +535,7 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
 #pragma unroll
       for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sa[kb][j]);
     }
-    if constexpr (CORR) {
+    if constexpr (CORR && decltype(chk)::value) {
       float rm = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -533,7 +565,38 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     }
   };
   // P = 2^(S*scale*log2e - m) and T = P*R in fp16, their row sums, and the
-  // value products O^T += V^T P^T, A_r^T += V^T T^T of tile kt_.
+  // value products O^T += V^T P^T, A_r^T += V^T T^T of one tile.
+  // vfrag(fb, t): the V^T fragment of feature 16*fb + c16, positions 8*(4t + g4) .. +7.
+  // (For the checked pass; the walk's copy, `softmax_pv`, reads LDS directly, as
+  // `scores` does.)
+  auto softmax_pv_of = [&](auto vfrag, f32x4 (&sa)[4], f32x4 (&ra)[4]) {
+    const float m_use = m_run;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f16x8 pf, rf, tf;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pf[4 * hh + j] =
+              (_Float16)__builtin_amdgcn_exp2f(fmaf(sa[2 * t + hh][j], sl2, -m_use));
+          if constexpr (CORR) rf[4 * hh + j] = (_Float16)ra[2 * t + hh][j];
+        }
+      }
+      if constexpr (CORR) tf = pf * rf;
+      acc_l = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8, pf, acc_l, 0, 0, 0);
+      if constexpr (CORR)
+        acc_c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8, tf, acc_c, 0, 0, 0);
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        const f16x8 va = vfrag(fb, t);
+        acc_o[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pf, acc_o[fb], 0, 0, 0);
+        if constexpr (CORR)
+          acc_r[fb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, tf, acc_r[fb], 0, 0, 0);
+      }
+    }
+  };
+  // the same with V^T tile `vbuf` in LDS
   auto softmax_pv = [&](auto vbuf, f32x4 (&sa)[4], f32x4 (&ra)[4]) {
     const float m_use = m_run;
     const uint16_t* vs = FUSEV > 0 ? smem + 4 * LY::K_ELEMS
@@ -612,15 +675,15 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     load_k(min(kt_ + 2, t_end - 1), P, KHalf{}, KAll1{});
     load_v(min(kt_ + 1, t_end - 1), 1 - P);
     softmax_pv(par, cs, cr);
-    return tile_max(ns, nr, kt_ + 1, diag_next);
+    return tile_max(ns, nr, kt_ + 1, diag_next, kHotCheck{});
   };
 
   f32x4 sn[4], rn[4];     // the other score register set of the pipelined loop
   if constexpr (PIPE) {
     if (w_end > t_beg) {
       scores(std::integral_constant<int, 0>{}, sc, rc);
-      m_run = needs_mask(t_beg) ? tile_max(sc, rc, t_beg, std::true_type{})
-                                : tile_max(sc, rc, t_beg, std::false_type{});
+      m_run = needs_mask(t_beg) ? tile_max(sc, rc, t_beg, std::true_type{}, kHotCheck{})
+                                : tile_max(sc, rc, t_beg, std::false_type{}, kHotCheck{});
     }
     // iteration 0 overwrites K buffer 0: every wave must be done reading it
     __syncthreads();
@@ -652,8 +715,9 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         }
       } else if constexpr (FUSEV == 0) {
         scores(par, cs, cr);
-        const float m_tile = needs_mask(kt) ? tile_max(cs, cr, kt, std::true_type{})
-                                            : tile_max(cs, cr, kt, std::false_type{});
+        const float m_tile =
+            needs_mask(kt) ? tile_max(cs, cr, kt, std::true_type{}, kHotCheck{})
+                           : tile_max(cs, cr, kt, std::false_type{}, kHotCheck{});
         if (kt == t_beg) m_run = m_tile;        // accumulators are still zero
         rescale_to(m_tile);
         softmax_pv(par, cs, cr);
@@ -666,8 +730,9 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       if (wave_u < FUSEV) {
         if (kt < w_end) {
           scores(par, cs, cr);
-          const float m_tile = needs_mask(kt) ? tile_max(cs, cr, kt, std::true_type{})
-                                              : tile_max(cs, cr, kt, std::false_type{});
+          const float m_tile =
+              needs_mask(kt) ? tile_max(cs, cr, kt, std::true_type{}, kHotCheck{})
+                             : tile_max(cs, cr, kt, std::false_type{}, kHotCheck{});
           if (kt == t_beg) m_run = m_tile;      // accumulators are still zero
           rescale_to(m_tile);
         }
@@ -688,6 +753,45 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   for (int kt = t_beg; kt < t_end; kt += 2) {
     iteration(kt, std::integral_constant<int, 0>{}, sc, rc, sn, rn);
     if (kt + 1 < t_end) iteration(kt + 1, std::integral_constant<int, 1>{}, sn, rn, sc, rc);
+  }
+
+  // Without FUSEV the walk above holds no |R| check.  fp16 carries R and T = P*R
+  // with the same relative precision at any magnitude it can represent; past its
+  // range R or T becomes infinite, and then the row's c (the sum of its T on the
+  // matrix cores) can only end as +-inf or NaN.  A wave with such a row walks its
+  // key tiles again, with the check, reading K and V^T straight from memory (its
+  // own pass, no LDS and no barrier): the check scales a row's R by a power of two
+  // before it can overflow, exactly, since Eq. 2 is linear in rho.
+  if constexpr (CORR && FUSEV == 0) {
+    if (__any(!__builtin_isfinite(acc_c[0]))) {
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        acc_o[fb] = f32x4{};
+        acc_r[fb] = f32x4{};
+      }
+      acc_l = f32x4{};
+      acc_c = f32x4{};
+      m_run = kMinit;
+      r_exp = 0.f;
+      for (int kt = t_beg; kt < w_end; ++kt) {
+        // key rows past the end read as zeros, as the tile loads give them
+        scores_of([&](int kb, int kk) {
+          const int row = kt * PF_BC + 16 * kb + c16;
+          return row < n_k ? *reinterpret_cast<const bf16x8*>(kh + (size_t)row * D + 32 * kk + 8 * g4)
+                           : bf16x8{};
+        }, sc, rc);
+        const float m_tile =
+            needs_mask(kt) ? tile_max(sc, rc, kt, std::true_type{}, std::true_type{})
+                           : tile_max(sc, rc, kt, std::false_type{}, std::true_type{});
+        if (kt == t_beg) m_run = m_tile;          // accumulators are still zero
+        rescale_to(m_tile);
+        softmax_pv_of([&](int fb, int t) {
+          // staged V^T tile kt: [D][64] fp16, unswizzled in memory
+          return *reinterpret_cast<const f16x8*>(vth + (size_t)kt * (D * PF_BC) +
+                                                 (size_t)(16 * fb + c16) * PF_BC + 8 * (4 * t + g4));
+        }, sc, rc);
+      }
+    }
   }
 
   // epilogue: o = o_sa - g (u - o_sa * rbar), o_sa = O/l, u = A_r/l, rbar = c/l

@@ -267,6 +267,78 @@ def test_large_rho_is_rescaled_exactly(d):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("i0", [37, 299])
+def test_one_large_rho_row_leaves_the_others_bit_identical(d, i0):
+    """One row whose |<rho,k>| exceeds fp16's range among ordinary rows: its R
+    overflows the fp16 products unless scaled, so the kernel takes the checked
+    pass for its 16-row block, which scales that row only.  Every other row (those
+    of the same block included) must come out bit-identical to a run without it,
+    and the row itself within its rounding bound of the oracle."""
+    B, H, L = 1, 2, 300
+    inp = wl.prefill_inputs(B, H, L, d, "bf16", seed=790 + d, device="cuda", rho_std=0.5,
+                            gate=("uniform", 0.2, 1.0))
+    base = _run(inp)
+    inp["rho"][0, 1, i0] = (inp["rho"][0, 1, i0].float() * (4e5 / d ** 0.5)).to(torch.bfloat16)
+    out = _run(inp)
+    keep = np.ones((B, H, L), bool)
+    keep[0, 1, i0] = False
+    assert np.array_equal(out[keep], base[keep])
+    assert np.isfinite(out).all()
+    h = {k: _host(x).double().numpy() for k, x in inp.items()}
+    rmax = float(np.abs(h["k"][0, 1, : i0 + 1] @ h["rho"][0, 1, i0]).max())
+    assert rmax > 65520                     # R itself overflows fp16 unscaled
+    ref = po.prefill_rows(h["q"], h["k"], h["v"], h["rho"], h["gate"], 0, 1, [i0])
+    bnd = _row_bound(h["q"][0, 1, : i0 + 1], h["k"][0, 1, : i0 + 1], h["v"][0, 1, : i0 + 1],
+                     h["rho"][0, 1, : i0 + 1], float(h["gate"][1]), 1.0 / np.sqrt(d),
+                     TOL["bf16"])[i0]
+    err = np.abs(out[0, 1, i0] - ref[0])
+    print(f"d{d} row {i0}: max |<rho,k>| {rmax:.3e}, max-abs {err.max():.3e}, "
+          f"max error/bound {(err / bnd).max():.3f}", flush=True)
+    assert np.all(err <= bnd)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_large_rho_training_statistics(d):
+    """The training forward with |<rho,k>| past fp16's range: the same output as
+    the inference kernel (bit-identical), the log partition function within
+    1e-3, and rbar and the correction vector within their rounding bounds (the
+    bound of the output's correction without the gate)."""
+    plx = _plx()
+    B, H, L = 1, 2, 200
+    inp = wl.prefill_inputs(B, H, L, d, "bf16", seed=800 + d, device="cuda", rho_std=1.0,
+                            gate=("uniform", 0.2, 1.0))
+    inp["rho"][:, 0] = (inp["rho"][:, 0].float() * (6e4 / d ** 0.5)).to(torch.bfloat16)
+    out, lse, rbar, corr = plx.prefill_train(inp["q"], inp["k"], inp["v"], inp["rho"],
+                                             inp["gate"])
+    plain = plx.prefill(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain)
+    h = {k: _host(x).double().numpy() for k, x in inp.items()}
+    assert np.abs(np.einsum("id,jd->ij", h["rho"][0, 0], h["k"][0, 0])).max() > 65520
+    ref = po.prefill_train(h["q"], h["k"], h["v"], h["rho"], h["gate"])
+    lse_h, rbar_h, corr_h = (t.cpu().double().numpy() for t in (lse, rbar, corr))
+    assert np.isfinite(corr_h).all() and np.isfinite(rbar_h).all()
+    assert float(np.abs(lse_h - ref["lse"]).max()) <= 1e-3
+    scale = 1.0 / np.sqrt(d)
+    for hh in range(H):
+        q, k, v, rho = (h[n][0, hh] for n in ("q", "k", "v", "rho"))
+        S = np.where(np.tril(np.ones((L, L), bool)), scale * (q @ k.T), -np.inf)
+        W = np.exp(S - S.max(1, keepdims=True))
+        W /= W.sum(1, keepdims=True)
+        R = np.abs(rho @ k.T)
+        # rbar = sum_j w_j r_j: each term within 4 roundings of 2^-11
+        bnd_r = TOL["bf16"] + 4 * 2.0 ** -11 * (W * R).sum(1)
+        bnd_c = _row_bound(q, k, v, rho, 1.0, scale, TOL["bf16"])
+        er = np.abs(rbar_h[0, hh] - ref["rbar"][0, hh])
+        ec = np.abs(corr_h[0, hh] - ref["corr"][0, hh])
+        print(f"train large rho d{d} head {hh}: max |rbar| {np.abs(ref['rbar'][0, hh]).max():.3e}"
+              f" err/bound {(er / bnd_r).max():.3f}; corr err/bound {(ec / bnd_c).max():.3f}",
+              flush=True)
+        assert np.all(er <= bnd_r)
+        assert np.all(ec <= bnd_c)
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_value_beyond_fp16_range_stays_in_its_rows(d):
     """A value past fp16's range at key j (clamped to +-65504 in the fp16 copy)
     must not change any row that does not attend it: rows i < j, including those
