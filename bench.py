@@ -59,6 +59,7 @@ sys.path.insert(0, ROOT)
 METRIC = ("Parallax decode HBM GB/s (% of peak) + prefill TFLOP/s (% bf16 MFMA peak)")
 PEAK_MFMA_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0               # MI355X HBM3E, published
+SWEEP_AHEAD = 200000                # spin cycles queued before each timed sweep call
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {   # the files whose text determines each kernel's code
     "prefill_bf16_kernel": ["parallax_local_linear_amd/csrc/prefill_bf16.hip",
@@ -118,15 +119,23 @@ def _median(xs):
 
 
 class Timer:
-    """Per-label lists of HIP-event pairs recorded on the current stream."""
+    """Per-label lists of HIP-event pairs recorded on the current stream.
 
-    def __init__(self, torch):
+    With `ahead` > 0 every timed call is queued behind a spin kernel of that many
+    GPU clock cycles, so that the host has submitted the call and its closing
+    event before the GPU reaches the opening one: the pair then brackets GPU
+    time only, not the host's submission of a call of a few microseconds."""
+
+    def __init__(self, torch, ahead=0):
         self.torch = torch
         self.ev = {}
+        self.ahead = ahead
 
     def run(self, label, fn):
         t = self.torch
         a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        if self.ahead:
+            t.cuda._sleep(self.ahead)
         a.record()
         fn()
         b.record()
@@ -529,15 +538,16 @@ def softmax_relative_prefill(torch, plx, wl, inp, w, vt, pout, steps=10):
             "flops": {"parallax": fl, "softmax": fl / 2}}
 
 
-def softmax_relative_decode(torch, plx, wl, inp, w, steps=10):
+def softmax_relative_decode(torch, plx, wl, inp, w, steps=10, ahead=0):
     """Parallax decode step against the softmax-only decode step (split pass and
-    combine each, same split size and workspace), alternating launch by launch."""
+    combine each, same split size and workspace), alternating launch by launch
+    (`ahead`: see Timer)."""
     B, H, Lmax, d = inp["kcache"].shape
     C = plx.decode_default_split(B, H, Lmax, d)
     ws = torch.empty(plx.decode_workspace_bytes(B, H, Lmax, d, C), dtype=torch.uint8,
                      device=inp["q"].device)
     out = torch.empty((B, H, d), dtype=torch.float32, device=inp["q"].device)
-    tm = Timer(torch)
+    tm = Timer(torch, ahead)
     for _ in range(steps + 2):
         tm.run("parallax", lambda: plx.decode(inp["q"], inp["kcache"], inp["vcache"], inp["rho"],
                                               inp["gate"], inp["seqlens"], split_keys=C,
@@ -561,7 +571,8 @@ def softmax_sweep(torch, plx, wl, dev, steps=3):
     """The pages' comparison with softmax attention across batch sizes and
     context lengths: the Parallax kernels and their softmax-only twins on a grid
     of shapes, alternating launch by launch (median of `steps` launches each
-    after one warm-up).  Prefill: H 16, L 1k-64k with B = max(1, 16k / L), at
+    after one warm-up), each call queued behind a 200k-cycle spin kernel so that
+    the events bracket GPU time (the smallest calls take 20 us).  Prefill: H 16, L 1k-64k with B = max(1, 16k / L), at
     d 64 and 128 (attend kernels; V staged once).  Decode: H 16, d 128,
     B 1 / 8 / 64 x L 8k / 32k / 128k (split pass + combine)."""
     pts = []
@@ -573,7 +584,7 @@ def softmax_sweep(torch, plx, wl, dev, steps=3):
                                     rho_std=0.1, gate=("uniform", 0.2, 1.0))
             vt = plx.prefill_stage_v(inp["v"])
             out = torch.empty((B, 16, L, d), dtype=torch.float32, device=dev)
-            tm = Timer(torch)
+            tm = Timer(torch, SWEEP_AHEAD)
             for _ in range(steps + 1):
                 tm.run("parallax", lambda: plx.prefill_attend(inp["q"], inp["k"], vt, inp["rho"],
                                                               inp["gate"], out=out))
@@ -594,7 +605,8 @@ def softmax_sweep(torch, plx, wl, dev, steps=3):
             log(f"sweep: decode B{B} H16 L{L} d128")
             inp = wl.decode_inputs(B, 16, L, 128, "bf16", seed=3100 + B, device=dev,
                                    rho_std=0.1)
-            r = softmax_relative_decode(torch, plx, wl, inp, None, steps=steps)
+            r = softmax_relative_decode(torch, plx, wl, inp, None, steps=steps,
+                                        ahead=SWEEP_AHEAD)
             pts.append({"kind": "decode", "B": B, "H": 16, "L": L, "d": 128,
                         "split_keys": r["split_keys"],
                         "parallax_ms": r["parallax_ms"], "softmax_ms": r["softmax_ms"],
