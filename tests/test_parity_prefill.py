@@ -298,6 +298,43 @@ def test_one_large_rho_row_leaves_the_others_bit_identical(d, i0):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+def test_t_overflow_with_r_in_fp16_range(d):
+    """R itself inside fp16's range (|r| about 2e4) while T = P*R is not: the
+    scores grow along the keys by about 3 (log2 units) per 64-key tile, so the
+    running max moves only every other tile and P reaches about 8 in between;
+    8 * 2e4 overflows fp16, and only T does.  Every row must be finite and within
+    its rounding bound of the oracle."""
+    B, H, L = 1, 1, 256
+    scale = 1.0 / np.sqrt(d)
+    step = 3.0 / (8.0 * scale * np.log2(np.e))        # k[:, 0] slope per tile, q[:, 0] = 8
+    q = torch.zeros((B, H, L, d))
+    k = torch.zeros((B, H, L, d))
+    rho = torch.zeros((B, H, L, d))
+    g = torch.Generator().manual_seed(810 + d)
+    q[..., 0] = 8.0
+    q[..., 2:] = 0.1 * torch.randn((B, H, L, d - 2), generator=g)
+    k[..., 0] = step * torch.arange(L, dtype=torch.float32) / 64
+    k[..., 1] = 100.0 + 10.0 * torch.randn((B, H, L), generator=g)
+    k[..., 2:] = torch.randn((B, H, L, d - 2), generator=g)
+    rho[..., 1] = 200.0
+    inp = {"q": q, "k": k, "v": torch.randn((B, H, L, d), generator=g), "rho": rho,
+           "gate": torch.full((H,), 0.7)}
+    inp = {n: (t.to(torch.bfloat16) if n != "gate" else t).cuda() for n, t in inp.items()}
+    out = _run(inp)
+    h = {n: _host(x).double().numpy() for n, x in inp.items()}
+    R = h["rho"][0, 0] @ h["k"][0, 0].T
+    assert np.abs(R).max() < 65504 and np.abs(R).max() > 4096
+    assert np.isfinite(out).all()
+    ref = po.prefill(h["q"], h["k"], h["v"], h["rho"], h["gate"])
+    bnd = _row_bound(h["q"][0, 0], h["k"][0, 0], h["v"][0, 0], h["rho"][0, 0],
+                     float(h["gate"][0]), scale, TOL["bf16"])
+    err = np.abs(out[0, 0] - ref[0, 0])
+    print(f"d{d}: max |r| {np.abs(R).max():.3e}, max-abs {err.max():.3e}, "
+          f"max error/bound {(err / bnd).max():.3f}", flush=True)
+    assert np.all(err <= bnd)
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_large_rho_training_statistics(d):
     """The training forward with |<rho,k>| past fp16's range: the same output as
     the inference kernel (bit-identical), the log partition function within
