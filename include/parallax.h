@@ -84,10 +84,13 @@ const char* parallax_last_error(void);
  *     unaffected (in particular, never NaN).  |v| <= 65280 is the exact range.
  *   - rho: no limit.  The softmax numerators P (kept <= 16) and
  *     r_ij = <rho_i,k_j> are rounded to fp16 and T = P*r is formed in fp16 for
- *     the value products; a row whose |r_ij| exceeds 2048 is scaled by a power
- *     of two before that rounding and unscaled in fp32 at the end, which is
- *     exact because Eq. 2 is linear in rho.  (Only an element of rho_i whose
- *     magnitude falls below 2^-126 after that scaling loses bits.) */
+ *     the value products.  When r or T of some row leaves fp16's range, the
+ *     16-row block holding that row is computed again with every row whose
+ *     |r_ij| exceeds 2048 scaled by a power of two before that rounding and
+ *     unscaled in fp32 at the end, which is exact because Eq. 2 is linear in
+ *     rho; the other rows of the block come out bit-identical.  (Only an element
+ *     of rho_i whose magnitude falls below 2^-126 after that scaling loses
+ *     bits.)  Such a block costs a second pass over its keys. */
 size_t parallax_prefill_workspace_bytes(int B, int H, int L, int d, int dtype);
 
 int parallax_prefill(const void* q, const void* k, const void* v, const void* rho,
