@@ -88,9 +88,9 @@ const char* parallax_last_error(void);
  *     16-row block holding that row is computed again with every row whose
  *     |r_ij| exceeds 2048 scaled by a power of two before that rounding and
  *     unscaled in fp32 at the end, which is exact because Eq. 2 is linear in
- *     rho; the other rows of the block come out bit-identical.  (Only an element
- *     of rho_i whose magnitude falls below 2^-126 after that scaling loses
- *     bits.)  Such a block costs a second pass over its keys. */
+ *     rho; the block's other rows come out bit-identical to the single pass.
+ *     (Only an element of rho_i whose magnitude falls below 2^-126 after that
+ *     scaling loses bits.)  Such a block costs a second pass over its keys. */
 size_t parallax_prefill_workspace_bytes(int B, int H, int L, int d, int dtype);
 
 int parallax_prefill(const void* q, const void* k, const void* v, const void* rho,
