@@ -508,14 +508,17 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
   // The tile walk checks |R| per tile only with the in-kernel V conversion
   // (FUSEV); the other kernels check each row once, after the walk (below).
   using kHotCheck = std::integral_constant<bool, (FUSEV > 0)>;
+  using kLanes = std::true_type;    // tile_max: the lane's own maximum
+  using kRows = std::false_type;    // tile_max: the row maximum (lanes exchanged)
   // Causal mask (the wave's last tile is its only diagonal tile) and the scaled
   // row max of one tile's scores; the four lanes that share a query combine.
   // With the correction, masked keys also get R = 0 (they never reach a row's
   // sums: neither their |R| nor an fp16 overflow of it may touch the row).  In
   // the checked walk (`chk`) the tile's |R| is held to kRMax before its fp16
   // conversion.
+  // (With `lanes`, the lane's own maximum, scaled, without the exchange.)
   auto tile_max = [&](f32x4 (&sa)[4], f32x4 (&ra)[4], int kt_, auto diag_c,
-                      auto chk) -> float {
+                      auto chk, auto lanes) -> float {
     if constexpr (decltype(diag_c)::value) {
       const int lim = pos0 + qi - kt_ * PF_BC - 4 * g4;   // key offset 16*kb + j kept iff <= lim
 #pragma unroll
@@ -544,9 +547,31 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
       }
       if (__any(rm > kRMax)) rescale_r(ra, rm);
     }
-    mx = lane_xor16(mx, Max{});
-    mx = lane_xor32(mx, Max{});
+    if constexpr (!decltype(lanes)::value) {
+      mx = lane_xor16(mx, Max{});
+      mx = lane_xor32(mx, Max{});
+    }
     return mx * sl2;
+  };
+  // The lazy rescale of a tile from its lanes' own (scaled) maxima, before the
+  // exchange between the four lanes of a query: a row's maximum passes the
+  // running max by more than the slack exactly when one of its lanes' does, so
+  // the exchange (two lane swaps) is needed only when a rescale is due.
+  auto rescale_lanes = [&](float m_lane) {
+    if (__any(m_lane > m_run + kRescaleSlack)) {
+      float mx = lane_xor16(m_lane, Max{});
+      mx = lane_xor32(mx, Max{});
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      acc_l *= alpha;
+      if constexpr (CORR) acc_c *= alpha;
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        acc_o[fb] *= alpha;
+        if constexpr (CORR) acc_r[fb] *= alpha;
+      }
+    }
   };
   // Lazy rescale: the running max only moves when some row's tile max exceeds
   // it by more than the slack, so P stays below 2^slack.
@@ -675,15 +700,15 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
     load_k(min(kt_ + 2, t_end - 1), P, KHalf{}, KAll1{});
     load_v(min(kt_ + 1, t_end - 1), 1 - P);
     softmax_pv(par, cs, cr);
-    return tile_max(ns, nr, kt_ + 1, diag_next, kHotCheck{});
+    return tile_max(ns, nr, kt_ + 1, diag_next, kHotCheck{}, kLanes{});
   };
 
   f32x4 sn[4], rn[4];     // the other score register set of the pipelined loop
   if constexpr (PIPE) {
     if (w_end > t_beg) {
       scores(std::integral_constant<int, 0>{}, sc, rc);
-      m_run = needs_mask(t_beg) ? tile_max(sc, rc, t_beg, std::true_type{}, kHotCheck{})
-                                : tile_max(sc, rc, t_beg, std::false_type{}, kHotCheck{});
+      m_run = needs_mask(t_beg) ? tile_max(sc, rc, t_beg, std::true_type{}, kHotCheck{}, kRows{})
+                                : tile_max(sc, rc, t_beg, std::false_type{}, kHotCheck{}, kRows{});
     }
     // iteration 0 overwrites K buffer 0: every wave must be done reading it
     __syncthreads();
@@ -709,15 +734,15 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
           const float m_next =
               needs_mask(kt + 1) ? pipe_step(kt, par, std::true_type{}, cs, cr, ns, nr)
                                  : pipe_step(kt, par, std::false_type{}, cs, cr, ns, nr);
-          rescale_to(m_next);
+          rescale_lanes(m_next);
         } else {
           softmax_pv(par, cs, cr);
         }
       } else if constexpr (FUSEV == 0) {
         scores(par, cs, cr);
         const float m_tile =
-            needs_mask(kt) ? tile_max(cs, cr, kt, std::true_type{}, kHotCheck{})
-                           : tile_max(cs, cr, kt, std::false_type{}, kHotCheck{});
+            needs_mask(kt) ? tile_max(cs, cr, kt, std::true_type{}, kHotCheck{}, kRows{})
+                           : tile_max(cs, cr, kt, std::false_type{}, kHotCheck{}, kRows{});
         if (kt == t_beg) m_run = m_tile;        // accumulators are still zero
         rescale_to(m_tile);
         softmax_pv(par, cs, cr);
@@ -731,8 +756,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         if (kt < w_end) {
           scores(par, cs, cr);
           const float m_tile =
-              needs_mask(kt) ? tile_max(cs, cr, kt, std::true_type{}, kHotCheck{})
-                             : tile_max(cs, cr, kt, std::false_type{}, kHotCheck{});
+              needs_mask(kt) ? tile_max(cs, cr, kt, std::true_type{}, kHotCheck{}, kRows{})
+                             : tile_max(cs, cr, kt, std::false_type{}, kHotCheck{}, kRows{});
           if (kt == t_beg) m_run = m_tile;      // accumulators are still zero
           rescale_to(m_tile);
         }
@@ -781,8 +806,8 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
                            : bf16x8{};
         }, sc, rc);
         const float m_tile =
-            needs_mask(kt) ? tile_max(sc, rc, kt, std::true_type{}, std::true_type{})
-                           : tile_max(sc, rc, kt, std::false_type{}, std::true_type{});
+            needs_mask(kt) ? tile_max(sc, rc, kt, std::true_type{}, std::true_type{}, kRows{})
+                           : tile_max(sc, rc, kt, std::false_type{}, std::true_type{}, kRows{});
         if (kt == t_beg) m_run = m_tile;          // accumulators are still zero
         rescale_to(m_tile);
         softmax_pv_of([&](int fb, int t) {
