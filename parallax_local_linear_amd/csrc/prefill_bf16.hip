@@ -740,11 +740,10 @@ void prefill_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict_
         }
       } else if constexpr (FUSEV == 0) {
         scores(par, cs, cr);
-        const float m_tile =
-            needs_mask(kt) ? tile_max(cs, cr, kt, std::true_type{}, kHotCheck{}, kRows{})
-                           : tile_max(cs, cr, kt, std::false_type{}, kHotCheck{}, kRows{});
-        if (kt == t_beg) m_run = m_tile;        // accumulators are still zero
-        rescale_to(m_tile);
+        // (the first tile always rescales: from m_run = kMinit to the row
+        // maxima, with zero accumulators)
+        rescale_lanes(needs_mask(kt) ? tile_max(cs, cr, kt, std::true_type{}, kHotCheck{}, kLanes{})
+                                     : tile_max(cs, cr, kt, std::false_type{}, kHotCheck{}, kLanes{}));
         softmax_pv(par, cs, cr);
       }
     }
