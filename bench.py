@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
                     [--no-softmax] [--no-backward] [--no-chunk] [--no-sweep]
+                    [--no-gemm-ref]
 
 One step is one pass of the whole hot path over resident synthetic inputs:
   1. bf16 causal prefill, B=4 H=16 L=4096 d=128 (V staging + fused kernel);
@@ -39,6 +40,9 @@ out (plain causal softmax attention) against the Parallax kernels on each
 workload, alternating the two launch by launch, and reports the time ratio;
 "softmax_sweep" does the same over batch sizes and context lengths (prefill
 L 1k-64k at d 64 and 128, decode B 1-64 x L 8k-128k).
+"mfma_reference" times the vendor bf16 GEMM (torch.matmul, 8192^3) alternately
+with the fused prefill kernel: on this power-limited chip it shows what share of
+the published MFMA peak bf16 matrix work reaches at all on the same box.
 The CPU baseline times the fp64 oracle on a bounded sample on the host.
 "checksums" holds the fp64 sum of every input tensor of the step.
 Prints exactly one JSON line on stdout.
@@ -273,6 +277,8 @@ def main():
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunked prefill timing")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the softmax-relative sweep over batch sizes and lengths")
+    ap.add_argument("--no-gemm-ref", action="store_true",
+                    help="skip the vendor bf16 GEMM timed beside the prefill kernel")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size kernel for scaling HBM byte counters)")
@@ -394,6 +400,9 @@ def main():
         res["calib_copy_bytes"] = {"read": n * 4, "write": n * 4}
         del src, dst
 
+    if not args.no_gemm_ref:
+        log("vendor GEMM reference")
+        res["mfma_reference"] = mfma_reference(torch, plx, wl, pin, wp, vt, pout)
     if not args.no_chunk:
         res["chunk"] = [chunk_block(torch, plx, wl, name, dev) for name in sorted(wl.CHUNK_WORKLOADS)]
     if not args.no_backward:
@@ -514,6 +523,50 @@ def backward_block(torch, plx, wl, inp, w, steps=10):
             "backward_TFLOP/s": round(2 * fl / b_ms / 1e9, 2),
             "backward_frac_of_mfma_peak": round(2 * fl / b_ms / 1e9 / PEAK_MFMA_BF16_TFLOPS, 4),
             "flops": {"forward": fl, "backward": 2 * fl}}
+
+
+def mfma_reference(torch, plx, wl, inp, w, vt, pout, steps=20, n=8192):
+    """What the device's bf16 matrix cores deliver to the vendor GEMM (torch.matmul
+    on two resident n x n bf16 matrices, which runs hipBLASLt) on this machine, beside
+    the fused prefill kernel: each back to back on its own, then alternating
+    launch by launch.  The chip is power-limited under MFMA load, so this
+    measures how much of the published 2.5 PF any bf16 MFMA work reaches here;
+    it is context for `roofline.frac`, not a replacement for its peak.  (The
+    GEMM's 384 MB of operands also evict the prefill's inputs from the last-level
+    cache, which the alternating figures include.)"""
+    dev = inp["q"].device
+    g = torch.Generator(device=dev).manual_seed(4321)
+    a = torch.randn((n, n), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    c = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+
+    def gemm():
+        torch.matmul(a, b, out=c)
+
+    def attend():
+        plx.prefill_attend(inp["q"], inp["k"], vt, inp["rho"], inp["gate"], out=pout)
+
+    tm = Timer(torch)
+    for _ in range(steps + 2):
+        tm.run("gemm_alone", gemm)
+    for _ in range(steps + 2):
+        tm.run("attend_alone", attend)
+    for _ in range(steps + 2):
+        tm.run("gemm_alt", gemm)
+        tm.run("attend_alt", attend)
+    torch.cuda.synchronize()
+    gfl = 2.0 * n ** 3
+    afl = wl.prefill_flops(w.B, w.H, w.L, w.d)
+    out = {"gemm": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt), fp32 accumulate, bf16 out",
+           "attend_workload": w.name}
+    for mode in ("alone", "alt"):
+        g_ms, a_ms = tm.ms("gemm_" + mode, 2), tm.ms("attend_" + mode, 2)
+        out[mode] = {"gemm_ms": round(g_ms, 4), "gemm_TFLOP/s": round(gfl / g_ms / 1e9, 1),
+                     "gemm_frac_of_peak": round(gfl / g_ms / 1e9 / PEAK_MFMA_BF16_TFLOPS, 4),
+                     "attend_ms": round(a_ms, 4), "attend_TFLOP/s": round(afl / a_ms / 1e9, 1),
+                     "attend_over_gemm": round(afl / a_ms / (gfl / g_ms), 4)}
+    del a, b, c
+    return out
 
 
 def softmax_relative_prefill(torch, plx, wl, inp, w, vt, pout, steps=10):
