@@ -1,5 +1,6 @@
-"""The prefill and the chunked-prefill serving step captured in HIP graphs
-(torch.cuda.CUDAGraph over the library's launches on the capture stream).  With
+"""The prefill, a chunked-prefill serving step and a training step (forward and
+backward) captured in HIP graphs (torch.cuda.CUDAGraph over the library's
+launches on the capture stream).  With
 the caller's workspace every call is kernel launches only (no allocation, no
 memset), so a step can be captured once and replayed with new inputs written
 into the same buffers.  Each replay must equal, bit for bit, the same calls run
@@ -120,3 +121,66 @@ def test_chunk_serving_step_graph_replays_match_eager(split):
         if prev is not None:
             assert not torch.equal(got, prev)
         prev = got
+
+
+def test_training_step_graph_replays_match_eager():
+    """The training forward (which saves the statistics) and the backward pass of a
+    ragged bf16 prefill in one graph; the captured forward's outputs are the
+    graph's own buffers.  Each replay's output and five gradients must equal the
+    eager calls' bit for bit."""
+    plx = _plx()
+    B, H, L, d = 1, 2, 300, 128
+    inp = wl.prefill_inputs(B, H, L, d, "bf16", seed=1620, device="cuda",
+                            gate=("uniform", 0.2, 1.0))
+    dout = torch.empty((B, H, L, d), dtype=torch.float32, device="cuda")
+    fws = torch.empty(plx.prefill_workspace_bytes(B, H, L, d), dtype=torch.uint8, device="cuda")
+    bws = torch.empty(plx.prefill_backward_workspace_bytes(B, H, L, d), dtype=torch.uint8,
+                      device="cuda")
+
+    def new_grads():
+        return tuple(torch.empty((B, H, L, d), dtype=torch.float32, device="cuda")
+                     for _ in range(4)) + (torch.empty(H, dtype=torch.float32, device="cuda"),)
+
+    grads_g = new_grads()
+    saved = {}
+
+    def step(grads=grads_g):
+        fwd = plx.prefill_train(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"],
+                                workspace=fws)
+        out, lse, rbar, corr = fwd
+        plx.prefill_backward(inp["q"], inp["k"], inp["v"], inp["rho"], inp["gate"], out, corr,
+                             lse, rbar, dout, grads=grads, workspace=bws)
+        return fwd
+
+    gen = torch.Generator(device="cuda").manual_seed(1621)
+    _fill(dout, gen)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        saved["fwd"] = step()
+    torch.cuda.synchronize()
+
+    prev = None
+    for r in range(3):
+        for name in ("q", "k", "v"):
+            _fill(inp[name], gen)
+        _fill(inp["rho"], gen, 0.1)
+        _fill(dout, gen)
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in saved["fwd"]] + [t.clone() for t in grads_g]
+        ref_grads = new_grads()
+        ref = list(step(ref_grads)) + list(ref_grads)
+        torch.cuda.synchronize()
+        print(f"training replay {r}: max |dq| {float(got[4].abs().max()):.3f}", flush=True)
+        for i, (x, y) in enumerate(zip(got, ref)):
+            assert torch.isfinite(x).all(), i
+            assert torch.equal(x, y), f"replay {r}: tensor {i} differs from the eager calls"
+        if prev is not None:
+            assert not torch.equal(got[4], prev)
+        prev = got[4]
